@@ -1,0 +1,10 @@
+"""CPU oracle for the CSA lightning-indexer top-k step (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  It shares no code with the HIP library.
+"""
+from .csa_oracle import (  # noqa: F401
+    decode_bf16, widen, visible_count, row_scores, order_desc, select_topk,
+    oracle_topk, oracle_threshold, oracle_interleaved, oracle_recall,
+    logit_threshold, exact_int_scores, exhaustive_topk,
+)
