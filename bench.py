@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA lightning-indexer top-k on one MI355X.
+
+A step is one csa_index_topk_prefill call over the V4-Flash-shaped prefill
+workload (B=1, S=16384 queries, m=4 so T=4096 compressed keys, H_I=64,
+d_I=128, top-k=2048; bf16 q/k ~ N(0,1)/sqrt(128), fp32 w ~ N(0,1)/8; causal)
+with inputs resident in HBM.  value = algorithmic prefill TFLOP/s: 2*H*D flops
+per (query, visible key) pair over rows with more visible keys than k.
+
+Also reported on the same JSON line:
+  roofline      the prefill kernel against the bf16 MFMA peak (HIP-event time
+                of each launch on the library's stream);
+  decode        the decode scan (B=32 x T=32768, k=2048) in GB/s against HBM
+                peak, K rotated over 4 copies so the 256 MB MALL cannot hold it;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer TFLOP/s (% bf16 MFMA peak) prefill; decode key-scan GB/s (% HBM peak)"
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _to_dev(p, torch, dev):
+    import numpy as np
+    if p["dtype"] == "bf16":
+        q = torch.from_numpy(p["q"].view(np.int16)).view(torch.bfloat16)
+        k = torch.from_numpy(p["k"].view(np.int16)).view(torch.bfloat16)
+    else:
+        q, k = torch.from_numpy(p["q"]), torch.from_numpy(p["k"])
+    return q.to(dev), k.to(dev), torch.from_numpy(p["w"]).to(dev)
+
+
+def _time_calls(torch, call, steps, warmup):
+    """Warm up, then time `steps` calls with HIP events on the current stream."""
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st)
+    for i in range(steps):
+        ev[i][0].record(st)
+        call(i)
+        ev[i][1].record(st)
+    t1.record(st)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return total_ms, sum(per) / len(per), per[len(per) // 2], per[0]
+
+
+def _traffic_record(kernel):
+    """HBM bytes per launch measured by rocprofv3 counters, if recorded for the
+    current kernel source (null once the kernel source changes)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "lightning_indexer_top_02_amd", "csrc", "csa_kernels.hip")
+    try:
+        rec = json.load(open(path)).get(kernel)
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec and rec.get("src_sha256") == sha:
+            return rec
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def bench_prefill(args, torch, L, csa_inputs, R):
+    dev = torch.device("cuda:0")
+    p = csa_inputs.config(2)
+    q, k, w = _to_dev(p, torch, dev)
+    topk = p["topk"]
+    prob = L.make_problem(q, k, w, m=p["m"], q_pos0=p["q_pos0"])
+    lib = L.load_library()
+    out = torch.empty((1, p["S_q"], topk), dtype=torch.int32, device=dev)
+    nws = L.workspace_size(L.OP_PREFILL, prob, topk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    pb = ctypes.byref(prob)
+    op, wp = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr())
+
+    def call(_):
+        s = lib.csa_index_topk_prefill(pb, topk, 0, op, None, wp, nws, stream)
+        if s != 0:
+            raise RuntimeError(lib.csa_last_error().decode())
+
+    need, allv = R.visible_pairs(p["S_q"], p["q_pos0"], p["m"], p["T"], topk)
+    flops = R.prefill_flops(p["H"], p["D"], need)
+    _log(f"prefill: {p['name']}; {flops / 1e9:.1f} GFLOP per step; workspace {nws / 2**20:.0f} MiB")
+    total_ms, avg_ms, med_ms, min_ms = _time_calls(torch, call, args.steps, args.warmup)
+    ms = total_ms / args.steps
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    res = dict(p=p, flops=flops, need=need, allv=allv, ms=ms, avg_ms=avg_ms, med_ms=med_ms, min_ms=min_ms,
+               peak_mem=peak_mem, ws=nws)
+    del q, k, w, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, torch, L, csa_inputs, R):
+    dev = torch.device("cuda:0")
+    p = csa_inputs.config(4)
+    q, k0, w = _to_dev(p, torch, dev)
+    ks = [k0] + [k0.clone() for _ in range(3)]          # 4 x 256 MiB of keys rotate through
+    topk = p["topk"]
+    lib = L.load_library()
+    probs = [L.make_problem(q, kk, w, m=p["m"], q_pos0=p["q_pos0"]) for kk in ks]
+    out = torch.empty((p["B"], 1, topk), dtype=torch.int32, device=dev)
+    nws = L.workspace_size(L.OP_DECODE, probs[0], topk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    op, wp = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr())
+    refs = [ctypes.byref(pp) for pp in probs]
+
+    def call(i):
+        s = lib.csa_index_topk_decode(refs[i % 4], topk, 0, op, None, wp, nws, stream)
+        if s != 0:
+            raise RuntimeError(lib.csa_last_error().decode())
+
+    nbytes = R.decode_bytes(p["B"], 1, p["T"], p["H"], p["D"], topk)
+    steps = max(args.steps * 4, 40)
+    total_ms, avg_ms, med_ms, min_ms = _time_calls(torch, call, steps, args.warmup)
+    ms = total_ms / steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    _log(f"decode: {p['name']}: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s")
+    del q, ks, k0, w, out, ws
+    torch.cuda.empty_cache()
+    return dict(value=round(gbps, 1), unit="GB/s", ms_per_call=round(ms, 5),
+                frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_call=nbytes,
+                calls=steps, kernels_per_call=2, key_copies_rotated=4,
+                workload="decode B=32 x 1 query, context 131072 (T=32768), H_I=64, d_I=128, k=2048, bf16")
+
+
+def cpu_baseline(seconds, R):
+    """Time the fp64 CPU oracle on a bounded, seeded sample of the prefill rows."""
+    import numpy as np
+
+    import csa_inputs
+    import oracle
+    p = csa_inputs.config(2)
+    needed = np.arange(p["S_q"])[np.array([min(i // 4 + 1, p["T"]) > p["topk"] for i in range(p["S_q"])])]
+    rng = np.random.default_rng(77)
+    order = rng.permutation(needed)
+    t0 = time.perf_counter()
+    oracle.oracle_topk(p, rows=order[:4])              # warm-up and calibration
+    per_row = (time.perf_counter() - t0) / 4
+    n = int(max(8, min(len(order), seconds / max(per_row, 1e-6))))
+    rows = np.sort(order[4:4 + n])
+    t0 = time.perf_counter()
+    oracle.oracle_topk(p, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = sum(min(int(r) // 4 + 1, p["T"]) for r in rows)
+    flops = R.prefill_flops(p["H"], p["D"], pairs)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = os.cpu_count()
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                seconds=round(dt, 2),
+                sample=f"{len(rows)} seeded random rows (of {len(needed)} needing selection) of the prefill "
+                       f"workload, {pairs} visible pairs, fp64 numpy oracle incl. its top-k")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(query rows shard across GPUs with no exchange; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import csa_inputs
+    import lightning_indexer_top_02_amd as L
+    from lightning_indexer_top_02_amd import roofline as R
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.load_library()
+
+    if args.only_decode:
+        print(json.dumps(bench_decode(args, torch, L, csa_inputs, R)), flush=True)
+        return
+    pf = bench_prefill(args, torch, L, csa_inputs, R)
+    dec = None if args.no_decode else bench_decode(args, torch, L, csa_inputs, R)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, R)
+
+    p = pf["p"]
+    tflops = pf["flops"] / (pf["ms"] * 1e-3) / 1e12
+    achieved = pf["flops"] / (pf["avg_ms"] * 1e-3) / 1e12
+    kname = "prefill_mfma_kernel<0>"
+    tr = _traffic_record(kname)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "V4-Flash-shaped prefill: B=1, S=16384 queries, m=4, T=4096 compressed keys, "
+                        "H_I=64, d_I=128, top-k=2048, causal, bf16 q/k, fp32 w",
+            "B": 1, "S_q": p["S_q"], "T": p["T"], "H_I": p["H"], "d_I": p["D"], "topk": p["topk"], "m": p["m"],
+            "flops_per_step": pf["flops"], "needed_pairs": pf["need"], "all_visible_pairs": pf["allv"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": kname,
+            "achieved": round(achieved, 2),
+            "peak": R.PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / R.PEAK_BF16_TFLOPS, 4),
+            "traffic": None if tr is None else tr["hbm_bytes_per_launch"],
+            "launch_ms_avg": round(pf["avg_ms"], 5),
+            "launch_ms_median": round(pf["med_ms"], 5),
+            "launch_ms_min": round(pf["min_ms"], 5),
+        },
+        "cpu_baseline": cpu,
+        "decode": dec,
+        "peak_mem_bytes": pf["peak_mem"],
+        "workspace_bytes": pf["ws"],
+        "materialised_score_tensor_bytes": R.materialised_score_bytes(1, p["S_q"], p["H"], p["T"]),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * csa_indexer.h -- C ABI of the MI355X (gfx950) CSA lightning-indexer top-k library.
+ *
+ * The operation.  DeepSeek-V3.2/V4 Compressed Sparse Attention (CSA) scores
+ * every compressed key with a "lightning indexer" and keeps the top-k keys of
+ * each query; a sparse attention kernel then reads only those keys
+ * ("StreamIndex: Memory-Bounded Compressed Sparse Attention via Streaming
+ * Top-k", abstract).  The indexer score is a per-head dot product of the query
+ * with the compressed key, passed through ReLU and fused across heads with
+ * per-head weights ("FlashMemory-DeepSeek-V4" machine review, axiom ledger,
+ * Eq. 4 as cited there; its "What carries the argument" section names ReLU as
+ * the native Lightning Indexer activation):
+ *
+ *     I[b,t,s] = sum_{j<H} w[b,t,j] * max( sum_{d<D} q[b,t,j,d] * k[b,s,d], 0 )
+ *
+ * Keys are compressed by ratio m (V4-Flash: m = 4, StreamIndex abstract); the
+ * query at absolute position t = q_pos0 + i sees keys s <= floor(t/m) (and
+ * s < T, s < kv_len[b]).  Selection is an exact top-k in the total order
+ * (score descending, key index ascending); -0.0 scores equal +0.0.  The
+ * library streams over keys and never forms the [B,S,H,T] score tensor that
+ * StreamIndex's abstract identifies as the memory problem (256 GB at
+ * S = 65,536, H = 64, m = 4).
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers unless marked (host).  Tensors
+ *    are packed row-major with the last dimension contiguous.
+ *  - The caller owns every buffer.  The library never allocates device memory
+ *    and never synchronises; work is enqueued on `hip_stream` (a hipStream_t;
+ *    NULL = the null stream) and the call returns at once.
+ *  - Argument validation is synchronous: on any error nothing is enqueued and
+ *    a non-zero csa_status is returned; csa_last_error() gives a message
+ *    (thread-local).  No C++ exception crosses this interface.
+ *  - Outputs are deterministic (bitwise identical for identical inputs and
+ *    launch configuration).  out_idx rows are SETS: entry order is unspecified
+ *    unless CSA_SORTED is given, which orders them by (score desc, index asc).
+ *    Rows with fewer than topk visible keys hold all visible keys first, then -1;
+ *    out_score (optional, may be NULL) holds the fp32 score of each entry and
+ *    -INFINITY for padding.
+ *  - Workspace: `ws` must hold at least csa_workspace_size(...) bytes for the
+ *    same problem, flags and device; it needs no initialisation and its
+ *    contents are undefined after the call.  ws may be NULL when that size is 0.
+ *  - Calls that share a workspace must not overlap (same stream = safe).
+ */
+#ifndef CSA_INDEXER_H
+#define CSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID = 1,     /* bad argument: null pointer, size <= 0, bad struct_size, ... */
+  CSA_ERR_UNSUPPORTED = 2, /* valid but not compiled: D, H, topk beyond limits, T >= 2^31 */
+  CSA_ERR_WORKSPACE = 3,   /* ws_bytes smaller than csa_workspace_size() */
+  CSA_ERR_DEVICE = 4       /* a HIP call or kernel launch failed */
+} csa_status;
+
+typedef enum { CSA_BF16 = 0, CSA_F32 = 1 } csa_dtype; /* dtype of q and k; w is always fp32 */
+
+enum {
+  CSA_SORTED = 1u,    /* order each output row by (score desc, index asc) */
+  CSA_NONCAUSAL = 2u  /* every key s < T (and < kv_len[b]) is visible */
+};
+
+/* Operation codes for csa_workspace_size. */
+enum {
+  CSA_OP_PREFILL = 0,
+  CSA_OP_DECODE = 1,
+  CSA_OP_THRESHOLD = 2,
+  CSA_OP_INTERLEAVED = 3,
+  CSA_OP_RECALL = 4
+};
+
+/* Limits of this build. */
+#define CSA_MAX_TOPK 4096   /* topk, cap and k_local */
+#define CSA_MAX_HEADS 128
+#define CSA_MAX_DECODE_SQ 16
+
+/* Problem description (host struct, passed by pointer).  Shapes:
+ *   q [B, S_q, H, D]  (dtype)      one query row per token, H indexer heads
+ *   k [B, T, D]       (dtype)      compressed keys
+ *   w [B, S_q, H]     fp32         per-query head weights
+ *   kv_len [B] int32 or NULL       extra per-sequence cap on visible keys
+ * D must be one of 32, 64, 128, 256; 1 <= H <= CSA_MAX_HEADS; T < 2^31.   */
+typedef struct {
+  uint32_t struct_size; /* must equal sizeof(csa_problem) */
+  int32_t dtype;        /* csa_dtype */
+  int32_t B, S_q, T, H, D;
+  int32_t m;            /* compression ratio, >= 1 */
+  int64_t q_pos0;       /* absolute position of query row 0, >= 0 */
+  const void* q;
+  const void* k;
+  const float* w;
+  const int32_t* kv_len;
+} csa_problem;
+
+/* Bytes of workspace the given operation needs on the current device.
+ * op: CSA_OP_*.  k_or_cap: topk (PREFILL, DECODE), cap (THRESHOLD) or k_local
+ * (INTERLEAVED); P: partitions (INTERLEAVED, else ignored).  For CSA_OP_RECALL
+ * pass prob = NULL; the size is 0.  bytes (host) receives the size. */
+csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap, int32_t P,
+                              uint32_t flags, size_t* bytes);
+
+/* Top-k key indices per query row (StreamIndex abstract: "the top-k are
+ * selected per query"), streaming over key tiles with a running per-query
+ * threshold; any S_q.  out_idx [B, S_q, topk] int32; out_score [B, S_q, topk]
+ * fp32 or NULL.  1 <= topk <= CSA_MAX_TOPK. */
+csa_status csa_index_topk_prefill(const csa_problem* prob, int32_t topk, uint32_t flags,
+                                  int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                                  void* hip_stream);
+
+/* Same contract and same result sets as csa_index_topk_prefill, for a few
+ * query rows per sequence against a long key range (decode: S_q <=
+ * CSA_MAX_DECODE_SQ).  The key scan is split across many workgroups and is
+ * bound by HBM bandwidth; the multi-layer-indexer blog post (rit.work) reports
+ * the indexer scan at about two thirds of a layer's attention-part time in
+ * 128K-context decode. */
+csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t flags,
+                                 int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                                 void* hip_stream);
+
+/* Sigmoid-threshold selection (FlashMemory-DeepSeek-V4 review, "What carries
+ * the argument": the Memory Indexer keeps keys whose sigmoid score passes a
+ * fixed 0.5 threshold instead of a fixed top-k).  Read as
+ * sigmoid(I + logit_bias) > prob_threshold, i.e. I > logit(tau) - bias
+ * (strict), decided on the fp32 score.  0 < prob_threshold < 1.
+ * out_count [B, S_q] int32: the true number of survivors (may exceed cap).
+ * out_idx [B, S_q, cap]: the min(cap, count) best survivors (score desc,
+ * index asc define "best"), then -1.  out_score optional. */
+csa_status csa_index_threshold_select(const csa_problem* prob, float prob_threshold,
+                                      float logit_bias, int32_t cap, uint32_t flags,
+                                      int32_t* out_idx, int32_t* out_count, float* out_score,
+                                      void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Interleaved relaxed selection on one GPU (Machine Press, "Million-Token
+ * Memory Without the Global Bottleneck": tokens laid out interleaved across
+ * devices, each device selects locally, the union is meant to cover the
+ * global top tokens).  Partition p < P holds keys s with s mod P == p and
+ * keeps its own top-k_local.  out_idx [B, S_q, P*k_local]: partition p's set
+ * at offset p*k_local, padded with -1.  out_score optional, same layout. */
+csa_status csa_index_topk_interleaved(const csa_problem* prob, int32_t P, int32_t k_local,
+                                      uint32_t flags, int32_t* out_idx, float* out_score,
+                                      void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Union recall of a selection against a reference selection, per row:
+ * |set(sel) ∩ set(ref)| / |set(ref)|, entries < 0 ignored; 1.0 when ref has
+ * no valid entry.  sel [rows, n_sel], ref [rows, n_ref] int32;
+ * out_recall [rows] fp32.  1 <= n_ref <= 8192, n_sel >= 1, T bounds valid
+ * indices (entries >= T are ignored).  ws unused (may be NULL). */
+csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref, int32_t n_ref,
+                          int64_t rows, int32_t T, float* out_recall, void* ws, size_t ws_bytes,
+                          void* hip_stream);
+
+const char* csa_status_str(csa_status s); /* static string, never NULL */
+const char* csa_last_error(void);         /* thread-local detail of this thread's last error */
+int csa_version(void);                    /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_INDEXER_H */

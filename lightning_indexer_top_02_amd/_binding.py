@@ -1,0 +1,243 @@
+"""ctypes binding of libcsa_indexer.so.
+
+Argument marshalling only: every step of the indexer runs in the library's
+HIP kernels.  Tensors are torch tensors on the current HIP device; outputs
+and workspace are allocated with torch (or passed in), and every call is
+enqueued on torch's current stream.  The library must be built
+(``python -m lightning_indexer_top_02_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcsa_indexer.so")
+
+CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = range(5)
+CSA_BF16, CSA_F32 = 0, 1
+CSA_SORTED, CSA_NONCAUSAL = 1, 2
+OP_PREFILL, OP_DECODE, OP_THRESHOLD, OP_INTERLEAVED, OP_RECALL = range(5)
+MAX_TOPK = 4096
+MAX_DECODE_SQ = 16
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class CsaProblem(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("S_q", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("m", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("w", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.POINTER(CsaProblem)
+_vp, _i32, _u32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "csa_workspace_size": (_i32, [ctypes.c_int, _P, _i32, _i32, _u32, ctypes.POINTER(_sz)]),
+    "csa_index_topk_prefill": (_i32, [_P, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_decode": (_i32, [_P, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_threshold_select": (_i32, [_P, _f32, _f32, _i32, _u32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_interleaved": (_i32, [_P, _i32, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
+    "csa_set_recall": (_i32, [_vp, _i32, _vp, _i32, ctypes.c_int64, _i32, _vp, _vp, _sz, _vp]),
+    "csa_status_str": (ctypes.c_char_p, [_i32]),
+    "csa_last_error": (ctypes.c_char_p, []),
+    "csa_version": (ctypes.c_int, []),
+}
+
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m lightning_indexer_top_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != CSA_OK:
+        lib = load_library()
+        raise CsaError(status, lib.csa_last_error().decode() or lib.csa_status_str(status).decode())
+
+
+def version() -> int:
+    return load_library().csa_version()
+
+
+# ---------------------------------------------------------------------------
+# torch plumbing
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_problem(q, k, w, m=4, q_pos0=0, kv_len=None):
+    """Check tensors and build the C problem struct (keeps the tensors alive)."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 3 or w.dim() != 3:
+        raise ValueError("expected q [B,S_q,H,D], k [B,T,D], w [B,S_q,H]")
+    B, S_q, H, D = q.shape
+    if k.shape[0] != B or k.shape[2] != D or tuple(w.shape) != (B, S_q, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} w {tuple(w.shape)}")
+    if q.dtype != k.dtype or q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q and k must share dtype bfloat16 or float32")
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    for name, t in (("q", q), ("k", k), ("w", w)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if kv_len is not None:
+        if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B or not kv_len.is_contiguous():
+            raise ValueError("kv_len must be a contiguous int32 GPU tensor of B entries")
+    p = CsaProblem()
+    p.struct_size = ctypes.sizeof(CsaProblem)
+    p.dtype = CSA_BF16 if q.dtype == torch.bfloat16 else CSA_F32
+    p.B, p.S_q, p.T, p.H, p.D = B, S_q, k.shape[1], H, D
+    p.m = int(m)
+    p.q_pos0 = int(q_pos0)
+    p.q, p.k, p.w = q.data_ptr(), k.data_ptr(), w.data_ptr()
+    p.kv_len = None if kv_len is None else kv_len.data_ptr()
+    return p
+
+
+def _flags(sorted_, causal):
+    return (CSA_SORTED if sorted_ else 0) | (0 if causal else CSA_NONCAUSAL)
+
+
+def workspace_size(op, prob, k_or_cap, P=1, flags=0) -> int:
+    n = _sz(0)
+    _check(load_library().csa_workspace_size(op, ctypes.byref(prob) if prob is not None else None,
+                                             int(k_or_cap), int(P), int(flags), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, device, ws=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def index_topk_prefill(q, k, w, topk, *, m=4, q_pos0=0, kv_len=None, sorted=False, causal=True,
+                       return_scores=False, out=None, out_score=None, workspace=None):
+    """Top-k key indices per query row: int32 [B, S_q, topk] (and fp32 scores)."""
+    torch = _torch()
+    prob = make_problem(q, k, w, m, q_pos0, kv_len)
+    flags = _flags(sorted, causal)
+    B, S_q = q.shape[0], q.shape[1]
+    idx = out if out is not None else torch.empty((B, S_q, topk), dtype=torch.int32, device=q.device)
+    sc = out_score if out_score is not None else (
+        torch.empty((B, S_q, topk), dtype=torch.float32, device=q.device) if return_scores else None)
+    ws = _workspace(workspace_size(OP_PREFILL, prob, topk, 1, flags), q.device, workspace)
+    _check(load_library().csa_index_topk_prefill(ctypes.byref(prob), int(topk), flags, _ptr(idx), _ptr(sc),
+                                                 _ptr(ws), _nbytes(ws), _stream_handle()))
+    return (idx, sc) if sc is not None else idx
+
+
+def index_topk_decode(q, k, w, topk, *, m=4, q_pos0=0, kv_len=None, sorted=False, causal=True,
+                      return_scores=False, out=None, out_score=None, workspace=None):
+    """Decode-shaped top-k (S_q <= 16): same result sets as index_topk_prefill."""
+    torch = _torch()
+    prob = make_problem(q, k, w, m, q_pos0, kv_len)
+    flags = _flags(sorted, causal)
+    B, S_q = q.shape[0], q.shape[1]
+    idx = out if out is not None else torch.empty((B, S_q, topk), dtype=torch.int32, device=q.device)
+    sc = out_score if out_score is not None else (
+        torch.empty((B, S_q, topk), dtype=torch.float32, device=q.device) if return_scores else None)
+    ws = _workspace(workspace_size(OP_DECODE, prob, topk, 1, flags), q.device, workspace)
+    _check(load_library().csa_index_topk_decode(ctypes.byref(prob), int(topk), flags, _ptr(idx), _ptr(sc),
+                                                _ptr(ws), _nbytes(ws), _stream_handle()))
+    return (idx, sc) if sc is not None else idx
+
+
+def index_threshold_select(q, k, w, cap, *, prob_threshold=0.5, logit_bias=0.0, m=4, q_pos0=0, kv_len=None,
+                           sorted=False, causal=True, return_scores=False, workspace=None):
+    """Keys with sigmoid(I + bias) > prob_threshold: (idx [B,S_q,cap], count [B,S_q][, scores])."""
+    torch = _torch()
+    prob = make_problem(q, k, w, m, q_pos0, kv_len)
+    flags = _flags(sorted, causal)
+    B, S_q = q.shape[0], q.shape[1]
+    idx = torch.empty((B, S_q, cap), dtype=torch.int32, device=q.device)
+    cnt = torch.empty((B, S_q), dtype=torch.int32, device=q.device)
+    sc = torch.empty((B, S_q, cap), dtype=torch.float32, device=q.device) if return_scores else None
+    ws = _workspace(workspace_size(OP_THRESHOLD, prob, cap, 1, flags), q.device, workspace)
+    _check(load_library().csa_index_threshold_select(ctypes.byref(prob), float(prob_threshold), float(logit_bias),
+                                                     int(cap), flags, _ptr(idx), _ptr(cnt), _ptr(sc), _ptr(ws),
+                                                     _nbytes(ws), _stream_handle()))
+    return (idx, cnt, sc) if sc is not None else (idx, cnt)
+
+
+def index_topk_interleaved(q, k, w, P, k_local, *, m=4, q_pos0=0, kv_len=None, sorted=False, causal=True,
+                           return_scores=False, out=None, workspace=None):
+    """Per-partition (s mod P) local top-k_local: int32 [B, S_q, P*k_local]."""
+    torch = _torch()
+    prob = make_problem(q, k, w, m, q_pos0, kv_len)
+    flags = _flags(sorted, causal)
+    B, S_q = q.shape[0], q.shape[1]
+    idx = out if out is not None else torch.empty((B, S_q, P * k_local), dtype=torch.int32, device=q.device)
+    sc = torch.empty((B, S_q, P * k_local), dtype=torch.float32, device=q.device) if return_scores else None
+    ws = _workspace(workspace_size(OP_INTERLEAVED, prob, k_local, P, flags), q.device, workspace)
+    _check(load_library().csa_index_topk_interleaved(ctypes.byref(prob), int(P), int(k_local), flags, _ptr(idx),
+                                                     _ptr(sc), _ptr(ws), _nbytes(ws), _stream_handle()))
+    return (idx, sc) if sc is not None else idx
+
+
+def set_recall(sel, ref, T, out=None):
+    """Per-row |set(sel) ∩ set(ref)| / |set(ref)| (entries < 0 ignored) as fp32 [rows]."""
+    torch = _torch()
+    if sel.dtype != torch.int32 or ref.dtype != torch.int32:
+        raise TypeError("sel and ref must be int32")
+    if not (sel.is_cuda and ref.is_cuda and sel.is_contiguous() and ref.is_contiguous()):
+        raise ValueError("sel and ref must be contiguous GPU tensors")
+    n_sel, n_ref = sel.shape[-1], ref.shape[-1]
+    rows = sel.numel() // n_sel
+    if ref.numel() // n_ref != rows:
+        raise ValueError("sel and ref must have the same number of rows")
+    rec = out if out is not None else torch.empty(rows, dtype=torch.float32, device=sel.device)
+    _check(load_library().csa_set_recall(_ptr(sel), int(n_sel), _ptr(ref), int(n_ref), int(rows), int(T),
+                                         _ptr(rec), None, 0, _stream_handle()))
+    return rec

@@ -1,0 +1,360 @@
+// C ABI of the CSA indexer library: argument validation, workspace sizing,
+// kernel dispatch and error reporting.  Nothing here allocates device memory
+// or synchronises; every launch goes to the caller's stream.
+#include "../../include/csa_indexer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "csa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+csa_status ok() {
+  g_last_error.clear();
+  return CSA_OK;
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool env_is(const char* name, const char* val) {
+  const char* e = std::getenv(name);
+  return e && std::strcmp(e, val) == 0;
+}
+
+csa_status validate_problem(const csa_problem* p) {
+  if (!p) return fail(CSA_ERR_INVALID, "problem pointer is NULL");
+  if (p->struct_size != sizeof(csa_problem))
+    return fail(CSA_ERR_INVALID, "struct_size %u != sizeof(csa_problem) %zu", p->struct_size,
+                sizeof(csa_problem));
+  if (p->dtype != CSA_BF16 && p->dtype != CSA_F32) return fail(CSA_ERR_INVALID, "unknown dtype %d", p->dtype);
+  if (p->B <= 0 || p->S_q <= 0 || p->T <= 0 || p->H <= 0 || p->D <= 0)
+    return fail(CSA_ERR_INVALID, "dimensions must be positive (B=%d S_q=%d T=%d H=%d D=%d)", p->B, p->S_q,
+                p->T, p->H, p->D);
+  if (p->m < 1) return fail(CSA_ERR_INVALID, "compression ratio m=%d < 1", p->m);
+  if (p->q_pos0 < 0) return fail(CSA_ERR_INVALID, "q_pos0=%lld < 0", (long long)p->q_pos0);
+  if (!p->q || !p->k || !p->w) return fail(CSA_ERR_INVALID, "q, k and w must not be NULL");
+  if (p->D != 32 && p->D != 64 && p->D != 128 && p->D != 256)
+    return fail(CSA_ERR_UNSUPPORTED, "D=%d not in {32,64,128,256}", p->D);
+  if (p->H > CSA_MAX_HEADS) return fail(CSA_ERR_UNSUPPORTED, "H=%d > %d", p->H, CSA_MAX_HEADS);
+  if ((long long)p->B * p->S_q > (1ll << 31) - 1) return fail(CSA_ERR_UNSUPPORTED, "B*S_q too large");
+  return CSA_OK;
+}
+
+csa_status validate_flags(uint32_t flags) {
+  if (flags & ~(uint32_t)(CSA_SORTED | CSA_NONCAUSAL)) return fail(CSA_ERR_INVALID, "unknown flag bits 0x%x", flags);
+  return CSA_OK;
+}
+
+csa_status validate_k(int32_t k, const char* what) {
+  if (k < 1) return fail(CSA_ERR_INVALID, "%s=%d < 1", what, k);
+  if (k > CSA_MAX_TOPK) return fail(CSA_ERR_UNSUPPORTED, "%s=%d > %d", what, k, CSA_MAX_TOPK);
+  return CSA_OK;
+}
+
+bool use_mfma(const csa_problem* p) {
+  if (env_is("CSA_FORCE_PATH", "generic")) return false;
+  return p->dtype == CSA_BF16 && p->H == 64 && p->D == 128;
+}
+
+// Candidate buffer capacity per query row: room for the top-k plus a batch of
+// appends between compactions.  CSA_CAND_CAP overrides (tests use it to force
+// frequent compactions); it is clamped to the minimum that keeps progress.
+int cand_capacity(int kk) {
+  const int lo = 2 * kk + 64;
+  long long c = std::max<long long>(4ll * kk, lo);
+  if (const char* e = std::getenv("CSA_CAND_CAP")) {
+    long long v = std::atoll(e);
+    if (v > 0) c = std::max<long long>(v, lo);
+  }
+  return (int)((c + 63) / 64 * 64);
+}
+
+struct PrefillPlan {
+  int nqb, n_items, ws_slots, C;
+  size_t cand_bytes, sort_bytes, total;
+};
+
+PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, uint32_t flags) {
+  PrefillPlan pl;
+  pl.nqb = (p->S_q + csa::PF_ROWS - 1) / csa::PF_ROWS;
+  long long items = (long long)p->B * pl.nqb * P;
+  pl.n_items = (int)std::min<long long>(items, (1ll << 31) - 1);
+  pl.ws_slots = (int)std::min<long long>(items, csa::PF_MAX_GRID);
+  pl.C = cand_capacity(kk);
+  pl.cand_bytes = align_up((size_t)pl.ws_slots * csa::PF_ROWS * pl.C * sizeof(unsigned long long));
+  pl.sort_bytes = (flags & CSA_SORTED) ? align_up((size_t)p->B * p->S_q * out_stride * sizeof(float)) : 0;
+  pl.total = pl.cand_bytes + pl.sort_bytes;
+  return pl;
+}
+
+// Decode path: bf16, H=64, D=128, few query rows.
+bool decode_fast(const csa_problem* p) { return use_mfma(p) && p->S_q <= CSA_MAX_DECODE_SQ; }
+
+struct DecodePlan {
+  int chunk, nsplit;
+  size_t score_bytes, sort_bytes, total;
+};
+
+DecodePlan plan_decode(const csa_problem* p, int kk, uint32_t flags) {
+  DecodePlan d;
+  d.chunk = 1024;
+  if (const char* e = std::getenv("CSA_DECODE_CHUNK")) {
+    int v = std::atoi(e);
+    if (v >= 256) d.chunk = (v + 255) / 256 * 256;
+  }
+  d.nsplit = (p->T + d.chunk - 1) / d.chunk;
+  d.score_bytes = align_up((size_t)p->B * p->S_q * p->T * sizeof(float));
+  d.sort_bytes = (flags & CSA_SORTED) ? align_up((size_t)p->B * p->S_q * kk * sizeof(float)) : 0;
+  d.total = d.score_bytes + d.sort_bytes;
+  return d;
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  return n;
+}
+
+int occupancy_cached(int mode, bool mfma, bool bf16) {
+  static std::mutex mu;
+  static int cache[64][3][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> g(mu);
+  int& c = cache[dev][mode][mfma][bf16];
+  if (c == 0) c = csa::prefill_blocks_per_cu(mode, mfma, bf16);
+  return c;
+}
+
+csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uint32_t flags,
+                              unsigned long long thr_fixed, int32_t* out_idx, float* out_score,
+                              int32_t* out_count, void* ws, size_t ws_bytes, void* stream) {
+  const int out_stride = kk * P;
+  const PrefillPlan pl = plan_prefill(p, kk, P, out_stride, flags);
+  if (ws_bytes < pl.total || (pl.total > 0 && !ws))
+    return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, pl.total);
+  const bool mfma = use_mfma(p);
+  const bool sorted = (flags & CSA_SORTED) != 0;
+  float* score_dst = out_score;
+  if (sorted && !score_dst) score_dst = (float*)((char*)ws + pl.cand_bytes);
+
+  csa::PrefillArgs a{};
+  a.q = p->q; a.k = p->k; a.w = p->w; a.kv_len = p->kv_len;
+  a.B = p->B; a.S_q = p->S_q; a.T = p->T; a.H = p->H; a.D = p->D; a.m = p->m;
+  a.q_pos0 = p->q_pos0;
+  a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
+  a.kk = kk; a.P = P; a.nqb = pl.nqb; a.n_items = pl.n_items;
+  a.thr_fixed = thr_fixed;
+  a.out_idx = out_idx; a.out_score = score_dst; a.out_count = out_count;
+  a.out_stride = out_stride;
+  a.cand = (unsigned long long*)ws;
+  a.C = pl.C;
+  a.need_scores = score_dst != nullptr;
+  a.bf16 = p->dtype == CSA_BF16;
+
+  const int resident = device_cus() * occupancy_cached(mode, mfma, a.bf16);
+  const int grid = std::max(1, std::min(pl.ws_slots, resident));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = csa::launch_prefill(a, mode, mfma, grid, st);
+  if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+  if (sorted) {
+    e = csa::launch_sort_rows(out_idx, score_dst, (long long)p->B * p->S_q * P, kk, st);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "sort launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_str(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID: return "CSA_ERR_INVALID: invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape or parameter not supported by this build";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace too small";
+    case CSA_ERR_DEVICE: return "CSA_ERR_DEVICE: HIP runtime or launch failure";
+  }
+  return "unknown csa_status";
+}
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+int csa_version(void) { return 100; }   // 0.1.0
+
+csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap, int32_t P, uint32_t flags,
+                              size_t* bytes) {
+  try {
+    if (!bytes) return fail(CSA_ERR_INVALID, "bytes pointer is NULL");
+    *bytes = 0;
+    if (op == CSA_OP_RECALL) return ok();
+    if (op < CSA_OP_PREFILL || op > CSA_OP_INTERLEAVED) return fail(CSA_ERR_INVALID, "unknown op %d", op);
+    csa_status s = validate_problem(prob);
+    if (s != CSA_OK) return s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(k_or_cap, "k")) != CSA_OK) return s;
+    int parts = 1;
+    if (op == CSA_OP_INTERLEAVED) {
+      if (P < 1) return fail(CSA_ERR_INVALID, "P=%d < 1", P);
+      if ((long long)P * k_or_cap > (1ll << 30)) return fail(CSA_ERR_UNSUPPORTED, "P*k_local too large");
+      parts = P;
+    }
+    if (op == CSA_OP_DECODE && prob->S_q > CSA_MAX_DECODE_SQ)
+      return fail(CSA_ERR_UNSUPPORTED, "decode needs S_q <= %d", CSA_MAX_DECODE_SQ);
+    if (op == CSA_OP_DECODE && decode_fast(prob)) {
+      *bytes = plan_decode(prob, k_or_cap, flags).total;
+    } else {
+      *bytes = plan_prefill(prob, k_or_cap, parts, k_or_cap * parts, flags).total;
+    }
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+csa_status csa_index_topk_prefill(const csa_problem* prob, int32_t topk, uint32_t flags, int32_t* out_idx,
+                                  float* out_score, void* ws, size_t ws_bytes, void* hip_stream) {
+  try {
+    csa_status s = validate_problem(prob);
+    if (s != CSA_OK) return s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(topk, "topk")) != CSA_OK) return s;
+    if (!out_idx) return fail(CSA_ERR_INVALID, "out_idx is NULL");
+    return run_prefill_family(prob, csa::MODE_TOPK, topk, 1, flags, 0ull, out_idx, out_score, nullptr, ws,
+                              ws_bytes, hip_stream);
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t flags, int32_t* out_idx,
+                                 float* out_score, void* ws, size_t ws_bytes, void* hip_stream) {
+  try {
+    csa_status s = validate_problem(prob);
+    if (s != CSA_OK) return s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(topk, "topk")) != CSA_OK) return s;
+    if (!out_idx) return fail(CSA_ERR_INVALID, "out_idx is NULL");
+    if (prob->S_q > CSA_MAX_DECODE_SQ)
+      return fail(CSA_ERR_UNSUPPORTED, "decode needs S_q <= %d (got %d)", CSA_MAX_DECODE_SQ, prob->S_q);
+    if (!decode_fast(prob))
+      return run_prefill_family(prob, csa::MODE_TOPK, topk, 1, flags, 0ull, out_idx, out_score, nullptr, ws,
+                                ws_bytes, hip_stream);
+    const DecodePlan d = plan_decode(prob, topk, flags);
+    if (ws_bytes < d.total || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, d.total);
+    const bool sorted = (flags & CSA_SORTED) != 0;
+    float* score_dst = out_score;
+    if (sorted && !score_dst) score_dst = (float*)((char*)ws + d.score_bytes);
+    csa::DecodeArgs a{};
+    a.q = prob->q; a.k = prob->k; a.w = prob->w; a.kv_len = prob->kv_len;
+    a.B = prob->B; a.S_q = prob->S_q; a.T = prob->T; a.m = prob->m; a.q_pos0 = prob->q_pos0;
+    a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
+    a.scores = (float*)ws;
+    a.chunk = d.chunk;
+    a.kk = topk;
+    a.out_idx = out_idx;
+    a.out_score = score_dst;
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = csa::launch_decode(a, d.nsplit, st);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+    if (sorted) {
+      e = csa::launch_sort_rows(out_idx, score_dst, (long long)prob->B * prob->S_q, topk, st);
+      if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "sort launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+csa_status csa_index_threshold_select(const csa_problem* prob, float prob_threshold, float logit_bias,
+                                      int32_t cap, uint32_t flags, int32_t* out_idx, int32_t* out_count,
+                                      float* out_score, void* ws, size_t ws_bytes, void* hip_stream) {
+  try {
+    csa_status s = validate_problem(prob);
+    if (s != CSA_OK) return s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(cap, "cap")) != CSA_OK) return s;
+    if (!out_idx || !out_count) return fail(CSA_ERR_INVALID, "out_idx and out_count must not be NULL");
+    if (!(prob_threshold > 0.0f && prob_threshold < 1.0f))
+      return fail(CSA_ERR_INVALID, "prob_threshold must be in (0,1)");
+    if (!std::isfinite(logit_bias)) return fail(CSA_ERR_INVALID, "logit_bias must be finite");
+    // sigma(I + bias) > tau  <=>  I > theta = log(tau/(1-tau)) - bias, decided on the
+    // fp32 score: I > theta  <=>  I >= f, f = the smallest float above theta.
+    const double t = (double)prob_threshold;
+    const double theta = std::log(t / (1.0 - t)) - (double)logit_bias;
+    float f = (float)theta;
+    if ((double)f <= theta) f = std::nextafter(f, INFINITY);
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if (u == 0x80000000u) u = 0u;
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const unsigned long long thr = (unsigned long long)ord << 32;
+    return run_prefill_family(prob, csa::MODE_THRESHOLD, cap, 1, flags, thr, out_idx, out_score, out_count, ws,
+                              ws_bytes, hip_stream);
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+csa_status csa_index_topk_interleaved(const csa_problem* prob, int32_t P, int32_t k_local, uint32_t flags,
+                                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                                      void* hip_stream) {
+  try {
+    csa_status s = validate_problem(prob);
+    if (s != CSA_OK) return s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(k_local, "k_local")) != CSA_OK) return s;
+    if (P < 1) return fail(CSA_ERR_INVALID, "P=%d < 1", P);
+    if ((long long)P * k_local > (1ll << 30)) return fail(CSA_ERR_UNSUPPORTED, "P*k_local too large");
+    if (!out_idx) return fail(CSA_ERR_INVALID, "out_idx is NULL");
+    return run_prefill_family(prob, csa::MODE_INTERLEAVED, k_local, P, flags, 0ull, out_idx, out_score, nullptr,
+                              ws, ws_bytes, hip_stream);
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref, int32_t n_ref, int64_t rows,
+                          int32_t T, float* out_recall, void* ws, size_t ws_bytes, void* hip_stream) {
+  (void)ws;
+  (void)ws_bytes;
+  try {
+    if (rows < 0) return fail(CSA_ERR_INVALID, "rows=%lld < 0", (long long)rows);
+    if (n_sel < 1 || n_ref < 1 || T < 1) return fail(CSA_ERR_INVALID, "n_sel, n_ref and T must be >= 1");
+    if (n_ref > 8192) return fail(CSA_ERR_UNSUPPORTED, "n_ref=%d > 8192", n_ref);
+    if (rows > 0 && (!sel || !ref || !out_recall)) return fail(CSA_ERR_INVALID, "sel, ref and out_recall must not be NULL");
+    if (rows > (1ll << 31) - 1) return fail(CSA_ERR_UNSUPPORTED, "too many rows");
+    hipError_t e = csa::launch_recall(sel, n_sel, ref, n_ref, rows, T, out_recall, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "recall launch failed: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,250 @@
+// Device primitives for the CSA indexer kernels (gfx950, wave64).
+//
+// Total order.  A selection key packs (score, index) into 64 bits so that a
+// larger key is a better key: the high word is the score mapped to an unsigned
+// integer with the same order (sign-flip transform used by radix sorts, after
+// turning -0.0 into +0.0 so that the two zeros tie), the low word is
+// 0xFFFFFFFF - index so that among equal scores the lower index wins.  All
+// keys are distinct, so "the k largest keys" is an exact, tie-free top-k.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef unsigned long long u64;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- keys
+
+__device__ __forceinline__ uint32_t score_order_bits(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;                      // -0.0 ties with +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_score(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ u64 make_key(float s, uint32_t idx) {
+  return ((u64)score_order_bits(s) << 32) | (u64)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ int key_index(u64 key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ float key_score(u64 key) { return order_bits_score((uint32_t)(key >> 32)); }
+
+// Smallest key whose score is >= s (any index).
+__device__ __forceinline__ u64 score_floor_key(float s) { return (u64)score_order_bits(s) << 32; }
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ u64 ballot(bool p) { return __ballot(p); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(u64 mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_bcast(T v, int src) {
+  return __shfl(v, src, WAVE);
+}
+
+__device__ __forceinline__ u64 wave_min_u64(u64 v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    u64 t = __shfl_xor(v, o, WAVE);
+    v = t < v ? t : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ u64 wave_max_u64(u64 v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    u64 t = __shfl_xor(v, o, WAVE);
+    v = t > v ? t : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// Inclusive prefix sum over lanes 0..63.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    int t = __shfl_up(v, o, WAVE);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int clz64(u64 x) { return __clzll((long long)x); }
+
+// ---------------------------------------------------------------- radix select
+//
+// Exact k-th largest key by most-significant-digit radix refinement.  The
+// digits start below the bits that all keys share (common prefix of min and
+// max), RB bits per pass, histogrammed in LDS.  A pass narrows to the bin that
+// holds rank k; it stops as soon as that whole bin is inside the top k, so
+// the result T satisfies |{key >= T}| == k exactly.
+
+constexpr int SEL_RB = 11;
+constexpr int SEL_BINS = 1 << SEL_RB;
+
+struct BinPick {
+  int bin;    // chosen bin
+  int above;  // keys in bins above it
+  int count;  // keys in it
+};
+
+// Given a histogram of `nb` bins (nb <= SEL_BINS) in LDS, find the bin that
+// holds rank `rank` counted from the top.  Whole wave calls it; result is
+// uniform.  Bins are scanned from the highest down.
+__device__ __forceinline__ BinPick wave_pick_bin(const uint32_t* hist, int nb, int rank) {
+  const int l = lane_id();
+  const int per = nb >= WAVE ? nb / WAVE : 1;
+  const int hi_bin = nb - 1 - l * per;            // this lane covers bins hi_bin .. hi_bin-per+1
+  int s = 0;
+  if (hi_bin >= 0) {
+    for (int j = 0; j < per; ++j) s += (int)hist[hi_bin - j];
+  }
+  const int incl = wave_incl_scan(s);
+  const int excl = incl - s;
+  const bool mine = hi_bin >= 0 && excl < rank && rank <= incl;
+  const u64 who = ballot(mine);
+  const int src = who ? (int)__builtin_ctzll(who) : 0;   // no lane: inconsistent counts, caller stops
+  int bin = 0, above = 0, cnt = 0;
+  if (mine) {
+    int cum = excl;
+    for (int j = 0; j < per; ++j) {
+      const int b = hi_bin - j;
+      const int h = (int)hist[b];
+      if (cum + h >= rank) {
+        bin = b; above = cum; cnt = h;
+        break;
+      }
+      cum += h;
+    }
+  }
+  BinPick r;
+  r.bin = wave_bcast(bin, src);
+  r.above = wave_bcast(above, src);
+  r.count = wave_bcast(cnt, src);
+  return r;
+}
+
+// Wave-level select over a key array in global memory written by this wave.
+// Requires n > k >= 1.  hist: this wave's SEL_BINS-entry LDS histogram.
+__device__ u64 wave_select_kth(const u64* buf, int n, int k, uint32_t* hist) {
+  const int l = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");   // own global stores -> visible to own loads
+  u64 lo = ~0ull, hi = 0ull;
+  for (int i = l; i < n; i += WAVE) {
+    const u64 x = buf[i];
+    lo = x < lo ? x : lo;
+    hi = x > hi ? x : hi;
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if (lo == hi) return lo;
+  int hi_bit = 64 - clz64(lo ^ hi);               // bits [hi_bit, 64) are common
+  u64 prefix = hi_bit >= 64 ? 0ull : (lo >> hi_bit);
+  int rank = k;
+  while (true) {
+    const int rb = hi_bit < SEL_RB ? hi_bit : SEL_RB;
+    const int shift = hi_bit - rb;
+    const int nb = 1 << rb;
+    const uint32_t dmask = (uint32_t)(nb - 1);
+    for (int b = l; b < nb; b += WAVE) hist[b] = 0u;
+    wave_lds_sync();
+    for (int i = l; i < n; i += WAVE) {
+      const u64 x = buf[i];
+      const bool match = hi_bit >= 64 || (x >> hi_bit) == prefix;
+      if (match) atomicAdd(&hist[(uint32_t)(x >> shift) & dmask], 1u);
+    }
+    wave_lds_sync();
+    const BinPick pk = wave_pick_bin(hist, nb, rank);
+    wave_lds_sync();
+    rank -= pk.above;
+    prefix = (prefix << rb) | (u64)pk.bin;
+    hi_bit = shift;
+    if (pk.count == rank || shift == 0) return prefix << shift;
+  }
+}
+
+// Block-level variant for one row of dense fp32 scores (implicit indices
+// idx = i), used by the decode select.  All NT threads call it; hist has
+// SEL_BINS entries; red has >= 2*NT/WAVE u64 entries of LDS.  Requires n > k >= 1.
+template <int NT>
+__device__ u64 block_select_kth_dense(const float* sc, int n, int k, uint32_t* hist, u64* red) {
+  const int tid = threadIdx.x;
+  const int l = lane_id(), wv = tid / WAVE;
+  constexpr int NW = NT / WAVE;
+  u64 lo = ~0ull, hi = 0ull;
+  for (int i = tid; i < n; i += NT) {
+    const u64 x = make_key(sc[i], (uint32_t)i);
+    lo = x < lo ? x : lo;
+    hi = x > hi ? x : hi;
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if (l == 0) { red[wv] = lo; red[NW + wv] = hi; }
+  __syncthreads();
+  lo = ~0ull; hi = 0ull;
+  for (int j = 0; j < NW; ++j) {
+    lo = red[j] < lo ? red[j] : lo;
+    hi = red[NW + j] > hi ? red[NW + j] : hi;
+  }
+  __syncthreads();
+  if (lo == hi) return lo;
+  int hi_bit = 64 - clz64(lo ^ hi);
+  u64 prefix = hi_bit >= 64 ? 0ull : (lo >> hi_bit);
+  int rank = k;
+  while (true) {
+    const int rb = hi_bit < SEL_RB ? hi_bit : SEL_RB;
+    const int shift = hi_bit - rb;
+    const int nb = 1 << rb;
+    const uint32_t dmask = (uint32_t)(nb - 1);
+    for (int b = tid; b < nb; b += NT) hist[b] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const u64 x = make_key(sc[i], (uint32_t)i);
+      const bool match = hi_bit >= 64 || (x >> hi_bit) == prefix;
+      if (match) atomicAdd(&hist[(uint32_t)(x >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const BinPick pk = wave_pick_bin(hist, nb, rank);
+      if (l == 0) { red[0] = (u64)pk.bin; red[1] = (u64)pk.above; red[2] = (u64)pk.count; }
+    }
+    __syncthreads();
+    const int bin = (int)red[0], above = (int)red[1], cnt = (int)red[2];
+    __syncthreads();
+    rank -= above;
+    prefix = (prefix << rb) | (u64)bin;
+    hi_bit = shift;
+    if (cnt == rank || shift == 0) return prefix << shift;
+  }
+}
+
+}  // namespace csa

@@ -1,0 +1,71 @@
+// Internal host/device interface between the C ABI (csa_api.cpp) and the
+// HIP kernels (csa_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+enum Mode { MODE_TOPK = 0, MODE_THRESHOLD = 1, MODE_INTERLEAVED = 2 };
+
+// Queries per workgroup in the prefill-family kernels: 4 waves x 2 query slots.
+constexpr int PF_ROWS = 8;
+constexpr int PF_THREADS = 256;
+// Upper bound on the persistent prefill grid (>= 2 workgroups per CU on 256 CUs);
+// each workgroup owns PF_ROWS candidate buffers in the workspace.
+constexpr int PF_MAX_GRID = 512;
+// Keys per LDS stage of the MFMA prefill kernel.
+constexpr int PF_KTILE = 64;
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const float* w;
+  const int32_t* kv_len;
+  int B, S_q, T, H, D, m;
+  long long q_pos0;
+  int causal;
+  int kk;               // topk / cap / k_local
+  int P;                // partitions (1 unless interleaved)
+  int nqb;              // query blocks per (b): ceil(S_q / PF_ROWS)
+  int n_items;          // B * nqb * P
+  unsigned long long thr_fixed;  // threshold mode: smallest surviving key
+  int32_t* out_idx;
+  float* out_score;     // may be null
+  int32_t* out_count;   // threshold mode
+  int out_stride;       // entries per output row (kk, or P*kk when interleaved)
+  unsigned long long* cand;      // [grid][PF_ROWS][C]
+  int C;                // candidate capacity per query row, >= 2*kk + 64
+  int need_scores;      // out_score != null
+  int bf16;             // element type of q and k: 1 = bf16, 0 = fp32
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const float* w;
+  const int32_t* kv_len;
+  int B, S_q, T, m;
+  long long q_pos0;
+  int causal;
+  float* scores;        // [B*S_q][T] fp32 workspace
+  int chunk;            // keys per workgroup along T (multiple of 256)
+  int kk;
+  int32_t* out_idx;
+  float* out_score;
+};
+
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_SEL_THREADS = 1024;
+
+// mfma: the bf16 H=64 D=128 MFMA kernel; otherwise the generic kernel for a.bf16.
+hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, hipStream_t st);
+// Resident workgroups per CU of the chosen prefill kernel (>= 1).
+int prefill_blocks_per_cu(int mode, bool mfma, bool bf16);
+hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st);
+hipError_t launch_sort_rows(int32_t* idx, float* score, long long rows, int len, hipStream_t st);
+hipError_t launch_recall(const int32_t* sel, int n_sel, const int32_t* ref, int n_ref,
+                         long long rows, int T, float* out, hipStream_t st);
+
+}  // namespace csa

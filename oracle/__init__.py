@@ -7,4 +7,5 @@ from .csa_oracle import (  # noqa: F401
     decode_bf16, widen, visible_count, row_scores, order_desc, select_topk,
     oracle_topk, oracle_threshold, oracle_interleaved, oracle_recall,
     logit_threshold, exact_int_scores, exhaustive_topk,
+    row_score_vector, RowScorer,
 )

@@ -124,6 +124,21 @@ class _Widened:
         return row_scores(self.q_row(b, i), self.k[b][:vis], self.w_row(b, i))
 
 
+def row_score_vector(prob, b, i):
+    """Float64 scores of query row i of sequence b against its visible keys."""
+    return _Widened(prob).scores(b, int(i))
+
+
+class RowScorer:
+    """Scores many rows of one problem, widening the keys once."""
+
+    def __init__(self, prob):
+        self._w = _Widened(prob)
+
+    def __call__(self, b, i):
+        return self._w.scores(b, int(i))
+
+
 # ---------------------------------------------------------------------------
 # selection
 

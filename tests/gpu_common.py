@@ -1,0 +1,90 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device and
+compare the HIP library's selections with the CPU oracle.
+
+Tolerance rule for bf16 inputs (fp32 accumulation on the GPU vs fp64 in the
+oracle): with rms = RMS of the row's visible oracle scores and
+floor = rms / 256,
+  * every returned score s: |I_gpu - I_ref| <= 2e-3 * max(|I_ref|, floor);
+  * an index may be in only one of the two sets only if its oracle score is
+    within 2e-3 * max(|v_n|, floor) of the oracle's n-th largest score v_n.
+Integer-valued inputs must match exactly (sets, and scores bitwise).
+"""
+import numpy as np
+import torch
+
+import oracle
+
+REL = 2e-3
+FLOOR_DIV = 256.0
+
+
+def to_device(prob, device="cuda"):
+    if prob["dtype"] == "bf16":
+        q = torch.from_numpy(np.ascontiguousarray(prob["q"]).view(np.int16)).view(torch.bfloat16)
+        k = torch.from_numpy(np.ascontiguousarray(prob["k"]).view(np.int16)).view(torch.bfloat16)
+    else:
+        q = torch.from_numpy(np.ascontiguousarray(prob["q"], dtype=np.float32))
+        k = torch.from_numpy(np.ascontiguousarray(prob["k"], dtype=np.float32))
+    w = torch.from_numpy(np.ascontiguousarray(prob["w"], dtype=np.float32))
+    kv = None
+    if prob.get("kv_len") is not None:
+        kv = torch.from_numpy(np.asarray(prob["kv_len"], dtype=np.int32)).to(device)
+    return q.to(device), k.to(device), w.to(device), kv
+
+
+def valid_prefix_ok(row, n):
+    """First n entries valid and distinct, the rest -1."""
+    head = row[:n]
+    return (head >= 0).all() and len(set(head.tolist())) == n and (row[n:] == -1).all()
+
+
+def check_exact(gpu_idx, ref_idx, gpu_score=None, ref_score=None):
+    """Integer inputs: identical sets per row (and identical scores per index)."""
+    g = np.asarray(gpu_idx)
+    r = np.asarray(ref_idx)
+    assert g.shape == r.shape
+    G = g.reshape(-1, g.shape[-1])
+    Rr = r.reshape(-1, r.shape[-1])
+    bad = [i for i in range(G.shape[0]) if sorted(G[i].tolist()) != sorted(Rr[i].tolist())]
+    assert not bad, f"{len(bad)} rows differ, first {bad[:5]}: gpu {sorted(G[bad[0]].tolist())[:12]} ref {sorted(Rr[bad[0]].tolist())[:12]}"
+    if gpu_score is not None:
+        GS = np.asarray(gpu_score).reshape(G.shape)
+        RS = np.asarray(ref_score).reshape(G.shape)
+        for i in range(G.shape[0]):
+            gm = dict(zip(G[i].tolist(), GS[i].tolist()))
+            rm = dict(zip(Rr[i].tolist(), RS[i].tolist()))
+            assert gm == rm, f"row {i} scores differ"
+
+
+def check_tolerance(prob, rows, gpu_idx, gpu_score, topk, b_list=None):
+    """bf16 inputs: the tolerance rule above, row by row (rows = query rows of gpu_idx[b, r])."""
+    scorer = oracle.RowScorer(prob)
+    B = prob["B"]
+    stats = dict(rows=0, swaps=0, max_rel=0.0)
+    for b in (range(B) if b_list is None else b_list):
+        for r, i in enumerate(rows):
+            I = scorer(b, i)
+            vis = I.shape[0]
+            n = min(topk, vis)
+            g = np.asarray(gpu_idx[b, r])
+            assert valid_prefix_ok(g, n), f"row {i}: bad padding/duplicates"
+            gs = g[:n]
+            assert (gs < vis).all(), f"row {i}: index beyond visible range"
+            if vis == 0:
+                continue
+            floor = float(np.sqrt(np.mean(I * I))) / FLOOR_DIV
+            ref = oracle.select_topk(I, n)
+            vn = I[ref].min() if n > 0 else 0.0
+            band = REL * max(abs(vn), floor)
+            diff = set(gs.tolist()) ^ set(ref.tolist())
+            for s in diff:
+                assert abs(I[s] - vn) <= band, f"row {i}: index {s} score {I[s]} outside band around v_n={vn}"
+            stats["swaps"] += len(diff) // 2
+            if gpu_score is not None:
+                sc = np.asarray(gpu_score[b, r][:n], dtype=np.float64)
+                err = np.abs(sc - I[gs])
+                lim = REL * np.maximum(np.abs(I[gs]), floor)
+                assert (err <= lim).all(), f"row {i}: score error {err.max()} beyond tolerance"
+                stats["max_rel"] = max(stats["max_rel"], float((err / np.maximum(np.abs(I[gs]), floor)).max()))
+            stats["rows"] += 1
+    return stats

@@ -1,0 +1,91 @@
+"""GPU parity of the interleaved-partition selection and the recall kernel."""
+import numpy as np
+import pytest
+
+import csa_inputs
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import lightning_indexer_top_02_amd as L  # noqa: E402
+from gpu_common import check_exact, check_tolerance, to_device  # noqa: E402
+
+
+def _say(msg):
+    print(f"[csa-test] {msg}", flush=True)
+
+
+def _integer(S_q=120, T=900, topk=128, seed=8, bf16=True):
+    p = csa_inputs.make_integer(S_q=S_q, T=T, H=64 if bf16 else 4, D=128 if bf16 else 32, m=4, topk=topk,
+                                q_pos0=3200, seed=seed, qk_range=2, w_range=2)
+    if bf16:
+        p["q"] = csa_inputs.f32_to_bf16_bits(p["q"])
+        p["k"] = csa_inputs.f32_to_bf16_bits(p["k"])
+        p["dtype"] = "bf16"
+    return p
+
+
+def _interleaved(p, P, kl, **kw):
+    q, k, w, kv = to_device(p)
+    out = L.index_topk_interleaved(q, k, w, P, kl, m=p["m"], q_pos0=p["q_pos0"], kv_len=kv, **kw)
+    torch.cuda.synchronize()
+    if isinstance(out, tuple):
+        return out[0], out[1].cpu().numpy()
+    return out, None
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+@pytest.mark.parametrize("P,kl", [(1, 128), (4, 20), (8, 16), (8, 200), (3, 7)])
+def test_interleaved_exact(P, kl, bf16):
+    p = _integer(bf16=bf16)
+    ref, ref_s = oracle.oracle_interleaved(p, P, kl)
+    idx, sc = _interleaved(p, P, kl, return_scores=True)
+    g = idx.cpu().numpy()
+    check_exact(g.reshape(1, -1, kl), ref.reshape(1, -1, kl), sc.reshape(1, -1, kl), ref_s.reshape(1, -1, kl))
+    # recall on the GPU vs the oracle's recall vs the closed form sum_p min(c_p, k_local) / n
+    gi, _, _ = oracle.oracle_topk(p)
+    q, k, w, _ = to_device(p)
+    glob = L.index_topk_prefill(q, k, w, p["topk"], m=p["m"], q_pos0=p["q_pos0"])
+    rec = L.set_recall(idx, glob, p["T"]).cpu().numpy()
+    ref_rec = oracle.oracle_recall(ref[0], gi[0])
+    assert np.allclose(rec, ref_rec, rtol=0, atol=1e-6)
+    for r in range(p["S_q"]):
+        G = [x for x in gi[0, r].tolist() if x >= 0]
+        cp = [sum(1 for s in G if s % P == part) for part in range(P)]
+        assert abs(rec[r] - sum(min(c, kl) for c in cp) / len(G)) < 1e-6
+    if P == 1:
+        assert np.allclose(rec, 1.0)
+
+
+def test_recall_kernel_edge_cases():
+    sel = torch.tensor([[1, 2, 3, -1], [5, 5, 6, 7], [9, 9, 9, 9], [0, 1, 2, 3]], dtype=torch.int32, device="cuda")
+    ref = torch.tensor([[3, 2, -1], [5, 8, 5], [-1, -1, -1], [1, 100, 2]], dtype=torch.int32, device="cuda")
+    rec = L.set_recall(sel, ref, 50).cpu().numpy()
+    assert rec.tolist() == [1.0, 0.5, 1.0, 1.0]
+
+
+def test_config5_interleaved_recall_sampled():
+    p = csa_inputs.config(5)
+    rows = csa_inputs.sample_rows(p["S_q"], 6, seed=55, must=(8191,))
+    _say("config 5 interleaved P=8 k_local=320 vs global top-2048")
+    q, k, w, _ = to_device(p)
+    il = L.index_topk_interleaved(q, k, w, 8, 320, m=4, q_pos0=p["q_pos0"])
+    glob = L.index_topk_prefill(q, k, w, 2048, m=4, q_pos0=p["q_pos0"])
+    rec = L.set_recall(il, glob, p["T"]).cpu().numpy()
+    _say(f"  recall mean={rec.mean():.6f} min={rec.min():.6f}")
+    il_np = il.cpu().numpy()
+    scorer = oracle.RowScorer(p)
+    ref = oracle.oracle_interleaved(p, 8, 320, rows=rows)[0]
+    for r_i, r in enumerate(rows):
+        I = scorer(0, r)
+        for part in range(8):
+            seg = il_np[0, r, part * 320:(part + 1) * 320]
+            rseg = ref[0, r_i, part * 320:(part + 1) * 320]
+            assert (seg >= 0).all() and (seg % 8 == part).all()
+            sub = np.arange(part, I.shape[0], 8)
+            vn = I[rseg].min()
+            floor = float(np.sqrt(np.mean(I * I))) / 256
+            for s in set(seg.tolist()) ^ set(rseg.tolist()):
+                assert abs(I[s] - vn) <= 2e-3 * max(abs(vn), floor)
+    assert rec.min() >= 0.99

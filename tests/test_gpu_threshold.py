@@ -1,0 +1,82 @@
+"""GPU parity of csa_index_threshold_select (sigmoid threshold instead of top-k)."""
+import math
+
+import numpy as np
+import pytest
+
+import csa_inputs
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import lightning_indexer_top_02_amd as L  # noqa: E402
+from gpu_common import REL, FLOOR_DIV, check_exact, to_device  # noqa: E402
+
+
+def _thr(prob, cap, tau, bias, **kw):
+    q, k, w, kv = to_device(prob)
+    idx, cnt, sc = L.index_threshold_select(q, k, w, cap, prob_threshold=tau, logit_bias=bias, m=prob["m"],
+                                            q_pos0=prob["q_pos0"], kv_len=kv, return_scores=True, **kw)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy(), sc.cpu().numpy()
+
+
+def _integer(S_q=200, T=600, seed=4, H=64, D=128, bf16=True):
+    p = csa_inputs.make_integer(S_q=S_q, T=T, H=H, D=D, m=4, topk=64, q_pos0=1500, seed=seed,
+                                qk_range=2, w_range=2)
+    if bf16:
+        p["q"] = csa_inputs.f32_to_bf16_bits(p["q"])
+        p["k"] = csa_inputs.f32_to_bf16_bits(p["k"])
+        p["dtype"] = "bf16"
+    return p
+
+
+@pytest.mark.parametrize("tau,bias,cap", [(0.5, 0.0, 600), (0.5, 0.0, 37), (0.5, 2.5, 128),
+                                          (1 / (1 + math.exp(-3.5)), 0.0, 256), (0.2, -1.0, 64)])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_threshold_exact_integer(tau, bias, cap, bf16):
+    p = _integer(bf16=bf16) if bf16 else _integer(H=4, D=32, bf16=False)
+    ref_i, ref_c, ref_s = oracle.oracle_threshold(p, tau, bias, cap)
+    idx, cnt, sc = _thr(p, cap, tau, bias)
+    assert (cnt == ref_c).all()
+    check_exact(idx, ref_i, sc, ref_s)
+
+
+def test_threshold_half_is_sign_test():
+    # tau = 0.5, bias = 0 keeps exactly the keys with I > 0 (strict)
+    p = _integer()
+    idx, cnt, _ = _thr(p, 600, 0.5, 0.0)
+    scorer = oracle.RowScorer(p)
+    for r in range(p["S_q"]):
+        I = scorer(0, r)
+        assert cnt[0, r] == int((I > 0).sum())
+
+
+def test_threshold_bf16_gaussian_tolerance():
+    p = csa_inputs.make_gaussian_bf16(1, 256, 2048, 64, 128, 4, 512, q_pos0=7000, seed=17)
+    tau, bias, cap = 0.5, -0.05, 512
+    idx, cnt, sc = _thr(p, cap, tau, bias)
+    theta = oracle.logit_threshold(tau, bias)
+    scorer = oracle.RowScorer(p)
+    for r in range(p["S_q"]):
+        I = scorer(0, r)
+        floor = float(np.sqrt(np.mean(I * I))) / FLOOR_DIV
+        band = REL * max(abs(theta), floor)
+        near = int((np.abs(I - theta) <= band).sum())
+        assert abs(int(cnt[0, r]) - int((I > theta).sum())) <= near
+        n = min(cap, int(cnt[0, r]))
+        sel = idx[0, r, :n]
+        assert (idx[0, r, n:] == -1).all() and len(set(sel.tolist())) == n
+        assert (I[sel] > theta - band).all()
+
+
+def test_threshold_nesting_gpu():
+    p = _integer()
+    prev = None
+    for tau in [0.3, 0.5, 0.7, 0.9]:
+        idx, cnt, _ = _thr(p, 600, tau, 0.0)
+        sets = [set(x for x in idx[0, r].tolist() if x >= 0) for r in range(p["S_q"])]
+        if prev is not None:
+            assert all(a <= b for a, b in zip(sets, prev))
+        prev = sets
