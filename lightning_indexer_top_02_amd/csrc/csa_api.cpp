@@ -78,12 +78,13 @@ bool use_mfma(const csa_problem* p) {
   return p->dtype == CSA_BF16 && p->H == 64 && p->D == 128;
 }
 
-// Candidate buffer capacity per query row: room for the top-k plus a batch of
-// appends between compactions.  CSA_CAND_CAP overrides (tests use it to force
+// Candidate buffer capacity per query row: the top-k plus as many appends
+// again between compactions (2k + 64: for k <= 2048 every select then runs on
+// keys held in registers).  CSA_CAND_CAP overrides (tests use it to force
 // frequent compactions); it is clamped to the minimum that keeps progress.
 int cand_capacity(int kk) {
   const int lo = 2 * kk + 64;
-  long long c = std::max<long long>(4ll * kk, lo);
+  long long c = lo;
   if (const char* e = std::getenv("CSA_CAND_CAP")) {
     long long v = std::atoll(e);
     if (v > 0) c = std::max<long long>(v, lo);

@@ -153,21 +153,76 @@ __device__ __forceinline__ BinPick wave_pick_bin(const uint32_t* hist, int nb, i
   return r;
 }
 
-// Wave-level select over a key array in global memory written by this wave.
-// Requires n > k >= 1.  hist: this wave's SEL_BINS-entry LDS histogram.
-__device__ u64 wave_select_kth(const u64* buf, int n, int k, uint32_t* hist) {
+// ---------------------------------------------------------------- register-resident select
+//
+// The same refinement over keys held in registers: x[j] is the key of element
+// j*WAVE + lane (wave version) or j*NT + tid (block version), 0 for empty
+// slots (0 is below every real key: its score word would have to be a NaN).
+// Keys are loaded once with all loads in flight; each pass only reads
+// registers and LDS.
+
+__device__ __forceinline__ float wave_min_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Linear score bins between the smallest and largest score of a key set.
+// Monotone in the score (IEEE subtraction, multiplication, fminf and the
+// truncating conversion never reverse an order), so every key in a higher
+// bin beats every key in a lower one: the bin holding rank k is the only one
+// that needs exact resolution.  Scores of typical rows share a few exponents,
+// which would crowd a first radix digit on raw bits into a handful of bins.
+struct LinBins {
+  float lo, scale;
+  __device__ __forceinline__ int operator()(u64 key) const {
+    return (int)fminf((key_score(key) - lo) * scale, (float)(SEL_BINS - 1));
+  }
+};
+
+__device__ __forceinline__ bool lin_bins_ok(float lo, float hi, LinBins& lb) {
+  const float range = hi - lo;
+  lb.lo = lo;
+  lb.scale = (float)SEL_BINS / range;
+  return range > 0.f && lb.scale > 0.f && lb.scale < __builtin_inff();
+}
+
+constexpr int WAVE_LIST = 256;    // keys of one linear bin resolved by a wave from LDS
+constexpr int BLOCK_LIST = 512;
+
+struct AnyKey {
+  __device__ __forceinline__ bool operator()(u64 v) const { return v != 0ull; }
+};
+struct InBin {
+  LinBins lb;
+  int bin;
+  __device__ __forceinline__ bool operator()(u64 v) const { return v != 0ull && lb(v) == bin; }
+};
+
+// Exact k-th largest of the keys in x accepted by `in` (more than k of them)
+// by most-significant-digit radix refinement from registers.
+template <int R, typename Pred>
+__device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, Pred in) {
   const int l = lane_id();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");   // own global stores -> visible to own loads
   u64 lo = ~0ull, hi = 0ull;
-  for (int i = l; i < n; i += WAVE) {
-    const u64 x = buf[i];
-    lo = x < lo ? x : lo;
-    hi = x > hi ? x : hi;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const u64 v = x[j];
+    if (j * WAVE < n && in(v)) {
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
   }
   lo = wave_min_u64(lo);
   hi = wave_max_u64(hi);
   if (lo == hi) return lo;
-  int hi_bit = 64 - clz64(lo ^ hi);               // bits [hi_bit, 64) are common
+  int hi_bit = 64 - clz64(lo ^ hi);
   u64 prefix = hi_bit >= 64 ? 0ull : (lo >> hi_bit);
   int rank = k;
   while (true) {
@@ -177,10 +232,13 @@ __device__ u64 wave_select_kth(const u64* buf, int n, int k, uint32_t* hist) {
     const uint32_t dmask = (uint32_t)(nb - 1);
     for (int b = l; b < nb; b += WAVE) hist[b] = 0u;
     wave_lds_sync();
-    for (int i = l; i < n; i += WAVE) {
-      const u64 x = buf[i];
-      const bool match = hi_bit >= 64 || (x >> hi_bit) == prefix;
-      if (match) atomicAdd(&hist[(uint32_t)(x >> shift) & dmask], 1u);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j * WAVE < n) {
+        const u64 v = x[j];
+        const bool match = in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix);
+        if (match) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
+      }
     }
     wave_lds_sync();
     const BinPick pk = wave_pick_bin(hist, nb, rank);
@@ -192,15 +250,260 @@ __device__ u64 wave_select_kth(const u64* buf, int n, int k, uint32_t* hist) {
   }
 }
 
-// Block-level variant for one row of dense fp32 scores (implicit indices
-// idx = i), used by the decode select.  All NT threads call it; hist has
-// SEL_BINS entries; red has >= 2*NT/WAVE u64 entries of LDS.  Requires n > k >= 1.
-template <int NT>
-__device__ u64 block_select_kth_dense(const float* sc, int n, int k, uint32_t* hist, u64* red) {
+// ---------------------------------------------------------------- streaming select
+//
+// The same selection over keys in global memory written earlier by this
+// wave (its candidate buffer), for use while the wave's MFMA operands occupy
+// the registers: every pass streams the buffer with 8 loads in flight per lane.
+
+constexpr int STREAM_BATCH = 16;
+
+template <typename F>
+__device__ __forceinline__ void wave_stream(const u64* buf, int n, F f) {
+  const int l = lane_id();
+  for (int base = 0; base < n; base += STREAM_BATCH * WAVE) {
+    u64 v[STREAM_BATCH];
+#pragma unroll
+    for (int j = 0; j < STREAM_BATCH; ++j) {
+      const int i = base + j * WAVE + l;
+      v[j] = i < n ? buf[i] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < STREAM_BATCH; ++j) f(v[j], base + j * WAVE);   // 0 = past the end
+  }
+}
+
+template <typename Pred>
+__device__ __forceinline__ u64 wave_radix_kth_stream(const u64* buf, int n, int k, uint32_t* hist, Pred in) {
+  const int l = lane_id();
+  u64 lo = ~0ull, hi = 0ull;
+  wave_stream(buf, n, [&](u64 v, int) {
+    if (in(v)) {
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+  });
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if (lo == hi) return lo;
+  int hi_bit = 64 - clz64(lo ^ hi);
+  u64 prefix = hi_bit >= 64 ? 0ull : (lo >> hi_bit);
+  int rank = k;
+  while (true) {
+    const int rb = hi_bit < SEL_RB ? hi_bit : SEL_RB;
+    const int shift = hi_bit - rb;
+    const int nb = 1 << rb;
+    const uint32_t dmask = (uint32_t)(nb - 1);
+    for (int b = l; b < nb; b += WAVE) hist[b] = 0u;
+    wave_lds_sync();
+    wave_stream(buf, n, [&](u64 v, int) {
+      if (in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix)) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
+    });
+    wave_lds_sync();
+    const BinPick pk = wave_pick_bin(hist, nb, rank);
+    wave_lds_sync();
+    rank -= pk.above;
+    prefix = (prefix << rb) | (u64)pk.bin;
+    hi_bit = shift;
+    if (pk.count == rank || shift == 0) return prefix << shift;
+  }
+}
+
+// Exact k-th largest key of buf[0..n) (n > k >= 1): linear-bin histogram,
+// gather of the bin holding rank k into `list`, radix resolution.  slo/shi
+// are per-lane bounds on the scores in the buffer (the caller tracked them
+// while appending; +inf/-inf where a lane saw none).
+__device__ __forceinline__ u64 wave_select_kth_stream(const u64* buf, int n, int k, uint32_t* hist, u64* list,
+                                                      float slo, float shi) {
+  const int l = lane_id();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // this wave's global stores -> its loads (same CU)
+  slo = wave_min_f32(slo);
+  shi = wave_max_f32(shi);
+  LinBins lb;
+  if (!lin_bins_ok(slo, shi, lb)) return wave_radix_kth_stream(buf, n, k, hist, AnyKey{});
+  for (int b = l; b < SEL_BINS; b += WAVE) hist[b] = 0u;
+  wave_lds_sync();
+  wave_stream(buf, n, [&](u64 v, int) {
+    if (v) atomicAdd(&hist[lb(v)], 1u);
+  });
+  wave_lds_sync();
+  const BinPick pk = wave_pick_bin(hist, SEL_BINS, k);
+  wave_lds_sync();
+  const int r = k - pk.above;
+  const InBin inb{lb, pk.bin};
+  if (pk.count > WAVE_LIST) return wave_radix_kth_stream(buf, n, r, hist, inb);
+  int w = 0;
+  wave_stream(buf, n, [&](u64 v, int) {
+    const bool in = inb(v);
+    const u64 m = ballot(in);
+    if (in) list[w + lanes_below(m)] = v;
+    w += __popcll(m);
+  });
+  wave_lds_sync();
+  constexpr int RL = WAVE_LIST / WAVE;
+  u64 y[RL];
+#pragma unroll
+  for (int j = 0; j < RL; ++j) {
+    const int i = j * WAVE + l;
+    y[j] = i < w ? list[i] : 0ull;
+  }
+  wave_lds_sync();
+  if (w == r) {
+    u64 mn = ~0ull;
+#pragma unroll
+    for (int j = 0; j < RL; ++j) mn = (y[j] && y[j] < mn) ? y[j] : mn;
+    return wave_min_u64(mn);
+  }
+  return wave_radix_kth(y, w, r, hist, AnyKey{});
+}
+
+// Block versions for the decode select: NT threads, R keys per thread
+// (x[j] = key of element j*NT + tid).  hist: SEL_BINS entries; red: >= 2*NT/WAVE
+// u64; list: BLOCK_LIST u64; cnt: one int of LDS.
+template <int NT, int R, typename Pred>
+__device__ __forceinline__ u64 block_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* red, Pred in) {
   const int tid = threadIdx.x;
   const int l = lane_id(), wv = tid / WAVE;
   constexpr int NW = NT / WAVE;
   u64 lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const u64 v = x[j];
+    if (j * NT < n && in(v)) {
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  __syncthreads();
+  if (l == 0) { red[wv] = lo; red[NW + wv] = hi; }
+  __syncthreads();
+  lo = ~0ull; hi = 0ull;
+  for (int j = 0; j < NW; ++j) {
+    lo = red[j] < lo ? red[j] : lo;
+    hi = red[NW + j] > hi ? red[NW + j] : hi;
+  }
+  __syncthreads();
+  if (lo == hi) return lo;
+  int hi_bit = 64 - clz64(lo ^ hi);
+  u64 prefix = hi_bit >= 64 ? 0ull : (lo >> hi_bit);
+  int rank = k;
+  while (true) {
+    const int rb = hi_bit < SEL_RB ? hi_bit : SEL_RB;
+    const int shift = hi_bit - rb;
+    const int nb = 1 << rb;
+    const uint32_t dmask = (uint32_t)(nb - 1);
+    for (int b = tid; b < nb; b += NT) hist[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j * NT < n) {
+        const u64 v = x[j];
+        const bool match = in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix);
+        if (match) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const BinPick pk = wave_pick_bin(hist, nb, rank);
+      if (l == 0) { red[0] = (u64)pk.bin; red[1] = (u64)pk.above; red[2] = (u64)pk.count; }
+    }
+    __syncthreads();
+    const int bin = (int)red[0], above = (int)red[1], cnt = (int)red[2];
+    __syncthreads();
+    rank -= above;
+    prefix = (prefix << rb) | (u64)bin;
+    hi_bit = shift;
+    if (cnt == rank || shift == 0) return prefix << shift;
+  }
+}
+
+template <int NT, int R>
+__device__ __forceinline__ u64 block_select_kth_regs(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* red, u64* list,
+                                     int* cnt) {
+  const int tid = threadIdx.x;
+  const int l = lane_id(), wv = tid / WAVE;
+  constexpr int NW = NT / WAVE;
+  float slo = __builtin_inff(), shi = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * NT < n && x[j]) {
+      const float s = key_score(x[j]);
+      slo = fminf(slo, s);
+      shi = fmaxf(shi, s);
+    }
+  }
+  slo = wave_min_f32(slo);
+  shi = wave_max_f32(shi);
+  float* fred = (float*)red;
+  __syncthreads();
+  if (l == 0) { fred[wv] = slo; fred[NW + wv] = shi; }
+  if (tid == 0) *cnt = 0;
+  __syncthreads();
+  slo = __builtin_inff(); shi = -__builtin_inff();
+  for (int j = 0; j < NW; ++j) {
+    slo = fminf(slo, fred[j]);
+    shi = fmaxf(shi, fred[NW + j]);
+  }
+  __syncthreads();
+  LinBins lb;
+  if (!lin_bins_ok(slo, shi, lb)) return block_radix_kth<NT>(x, n, k, hist, red, AnyKey{});
+  for (int b = tid; b < SEL_BINS; b += NT) hist[b] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * NT < n && x[j]) atomicAdd(&hist[lb(x[j])], 1u);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const BinPick pk = wave_pick_bin(hist, SEL_BINS, k);
+    if (l == 0) { red[0] = (u64)pk.bin; red[1] = (u64)pk.above; red[2] = (u64)pk.count; }
+  }
+  __syncthreads();
+  const int bin = (int)red[0], r = k - (int)red[1], bcnt = (int)red[2];
+  __syncthreads();
+  const InBin inb{lb, bin};
+  if (bcnt > BLOCK_LIST) return block_radix_kth<NT>(x, n, r, hist, red, inb);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * NT < n && inb(x[j])) list[atomicAdd(cnt, 1)] = x[j];   // order within the bin is irrelevant
+  }
+  __syncthreads();
+  if (wv == 0) {
+    constexpr int RL = BLOCK_LIST / WAVE;
+    u64 y[RL];
+#pragma unroll
+    for (int j = 0; j < RL; ++j) {
+      const int i = j * WAVE + l;
+      y[j] = i < bcnt ? list[i] : 0ull;
+    }
+    u64 T;
+    if (bcnt == r) {
+      u64 mn = ~0ull;
+#pragma unroll
+      for (int j = 0; j < RL; ++j) mn = (y[j] && y[j] < mn) ? y[j] : mn;
+      T = wave_min_u64(mn);
+    } else {
+      T = wave_radix_kth(y, bcnt, r, hist, AnyKey{});
+    }
+    if (l == 0) red[0] = T;
+  }
+  __syncthreads();
+  const u64 T = red[0];
+  __syncthreads();
+  return T;
+}
+
+// Block-level select over dense fp32 scores in global memory (implicit
+// indices idx = i), for rows too long for registers.  Requires n > k >= 1.
+template <int NT>
+__device__ __forceinline__ u64 block_select_kth_dense(const float* sc, int n, int k, uint32_t* hist, u64* red) {
+  const int tid = threadIdx.x;
+  const int l = lane_id(), wv = tid / WAVE;
+  constexpr int NW = NT / WAVE;
+  u64 lo = ~0ull, hi = 0ull;
+#pragma unroll 8
   for (int i = tid; i < n; i += NT) {
     const u64 x = make_key(sc[i], (uint32_t)i);
     lo = x < lo ? x : lo;
@@ -227,6 +530,7 @@ __device__ u64 block_select_kth_dense(const float* sc, int n, int k, uint32_t* h
     const uint32_t dmask = (uint32_t)(nb - 1);
     for (int b = tid; b < nb; b += NT) hist[b] = 0u;
     __syncthreads();
+#pragma unroll 8
     for (int i = tid; i < n; i += NT) {
       const u64 x = make_key(sc[i], (uint32_t)i);
       const bool match = hi_bit >= 64 || (x >> hi_bit) == prefix;

@@ -9,10 +9,10 @@ namespace csa {
 
 enum Mode { MODE_TOPK = 0, MODE_THRESHOLD = 1, MODE_INTERLEAVED = 2 };
 
-// Queries per workgroup in the prefill-family kernels: 4 waves x 2 query slots.
-constexpr int PF_ROWS = 8;
+// Queries per workgroup in the prefill-family kernels: 4 waves x 1 query row.
+constexpr int PF_ROWS = 4;
 constexpr int PF_THREADS = 256;
-// Upper bound on the persistent prefill grid (>= 2 workgroups per CU on 256 CUs);
+// Upper bound on the persistent prefill grid (2 workgroups per CU on 256 CUs);
 // each workgroup owns PF_ROWS candidate buffers in the workspace.
 constexpr int PF_MAX_GRID = 512;
 // Keys per LDS stage of the MFMA prefill kernel.
@@ -36,7 +36,7 @@ struct PrefillArgs {
   int32_t* out_count;   // threshold mode
   int out_stride;       // entries per output row (kk, or P*kk when interleaved)
   unsigned long long* cand;      // [grid][PF_ROWS][C]
-  int C;                // candidate capacity per query row, >= 2*kk + 64
+  int C;                // candidate capacity per query row, >= kk + 64
   int need_scores;      // out_score != null
   int bf16;             // element type of q and k: 1 = bf16, 0 = fp32
 };

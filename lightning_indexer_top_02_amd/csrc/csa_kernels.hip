@@ -5,13 +5,12 @@
 // per-query running top-k; the [B,S,H,T] score tensor is never formed.
 //
 // Prefill family (top-k, threshold, interleaved partitions):
-//   persistent grid; a workgroup owns PF_ROWS = 8 consecutive query rows, a
-//   wave owns 2 of them ("slots": lanes 0-31 -> slot 0, lanes 32-63 -> slot 1).
-//   Per key tile the wave produces one score per lane, filters it against the
-//   slot's running threshold key and appends survivors to the slot's candidate
-//   buffer in the workspace.  A full buffer is compacted to the exact top-k
-//   (radix select), which raises the threshold; at the end the exact top-k of
-//   the buffer is emitted.
+//   persistent grid; a workgroup owns PF_ROWS = 4 consecutive query rows,
+//   one per wave.  Per step the wave produces 64 (query, key) scores, one per
+//   lane, filters them against the query's running threshold key and appends
+//   survivors to the query's candidate buffer in the workspace.  A full
+//   buffer is compacted to the exact top-k (which raises the threshold); at
+//   the end the exact top-k of the buffer is emitted.
 // Decode: scores of a few queries against a long key range, split across
 //   many workgroups (HBM-bound), then one workgroup per row selects.
 #include "csa_device.hpp"
@@ -20,6 +19,10 @@
 namespace csa {
 
 // ============================================================ shared pieces
+
+// max(x, 0) as one integer max on the bits: negative floats (and -0.0) are
+// negative as int32, non-negative ones keep their order; -0.0 becomes +0.0.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ int row_visible(const PrefillArgs& a, int b, int row, int part) {
   if (row >= a.S_q) return 0;
@@ -34,93 +37,79 @@ __device__ __forceinline__ int row_visible(const PrefillArgs& a, int b, int row,
   return (int)v;
 }
 
-// Wave-uniform top-k state of a wave's two query slots.
-struct SlotPair {
-  u64* cand[2];
-  int cnt[2];
-  u64 thr[2];     // keys below thr[s] cannot enter slot s's top-k
-  int surv[2];    // threshold mode: keys >= thr_fixed seen
+// Top-k state of the wave's query row (wave-uniform except lo/hi).
+struct Slot {
+  u64* cand;     // candidate buffer (C keys)
+  int cnt;       // keys in it
+  u64 thr;       // keys below thr cannot enter the top-k
+  int surv;      // threshold mode: keys >= thr_fixed seen
+  float lo, hi;  // per lane: bounds on the scores this lane appended
 };
 
-// Keep the exact top-kk of buf[0..cnt) in place; returns the new threshold.
-__device__ u64 wave_compact(u64* buf, int cnt, int kk, uint32_t* hist) {
-  const int l = lane_id();
-  const u64 T = wave_select_kth(buf, cnt, kk, hist);
+// Keep the exact top-kk of buf[0..cnt) in place (cnt > kk); returns the new
+// append threshold (one above the kk-th key).  Streams the buffer: the
+// wave's MFMA operands stay in registers meanwhile.
+__device__ __forceinline__ u64 wave_compact(u64* buf, int cnt, int kk, uint32_t* hist, u64* list, float lo,
+                                           float hi) {
+  const u64 T = wave_select_kth_stream(buf, cnt, kk, hist, list, lo, hi);
   int w = 0;
-  for (int base = 0; base < cnt; base += WAVE) {
-    const int i = base + l;
-    const u64 x = i < cnt ? buf[i] : 0ull;
-    const bool keep = i < cnt && x >= T;
+  wave_stream(buf, cnt, [&](u64 v, int) {        // in order; writes never pass the reads
+    const bool keep = v >= T && v != 0ull;
     const u64 m = ballot(keep);
-    if (keep) buf[w + lanes_below(m)] = x;   // w + rank <= i: never ahead of the reads
+    if (keep) buf[w + lanes_below(m)] = v;
     w += __popcll(m);
-  }
+  });
   return T + 1ull;
 }
 
+// Offer one key per lane (valid lanes only) to the wave's query.
 template <int MODE>
-__device__ __forceinline__ void wave_offer(SlotPair& st, u64 key, bool valid, const PrefillArgs& a,
-                                           uint32_t* hist) {
-  const int l = lane_id();
-  const int slot = l >> 5;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (st.cnt[s] + 32 > a.C) {                       // make room: at most 32 appends per slot
-      u64 t = wave_compact(st.cand[s], st.cnt[s], a.kk, hist);
-      st.thr[s] = t > st.thr[s] ? t : st.thr[s];
-      st.cnt[s] = a.kk;
-    }
+__device__ __forceinline__ void wave_offer(Slot& st, float score, uint32_t idx, bool valid, const PrefillArgs& a,
+                                           uint32_t* hist, u64* list) {
+  if (st.cnt + WAVE > a.C) {                          // make room: at most 64 appends per offer
+    const u64 t = wave_compact(st.cand, st.cnt, a.kk, hist, list, st.lo, st.hi);
+    st.thr = t > st.thr ? t : st.thr;
+    st.cnt = a.kk;
+    st.lo = key_score(t - 1ull);                       // every survivor scores >= the kk-th
   }
-  if (MODE == MODE_THRESHOLD) {
-    const u64 ms = ballot(valid && key >= a.thr_fixed);
-    st.surv[0] += __popc((uint32_t)ms);
-    st.surv[1] += __popc((uint32_t)(ms >> 32));
-  }
-  const u64 thr = slot ? st.thr[1] : st.thr[0];
-  const bool keep = valid && key >= thr;
+  const u64 key = make_key(score, idx);
+  if (MODE == MODE_THRESHOLD) st.surv += __popcll(ballot(valid && key >= a.thr_fixed));
+  const bool keep = valid && key >= st.thr;
   const u64 m = ballot(keep);
-  const int n0 = __popc((uint32_t)m), n1 = __popc((uint32_t)(m >> 32));
   if (keep) {
-    const int pos = lanes_below(m) - (slot ? n0 : 0);
-    u64* dst = slot ? st.cand[1] : st.cand[0];
-    dst[(slot ? st.cnt[1] : st.cnt[0]) + pos] = key;
+    st.cand[st.cnt + lanes_below(m)] = key;
+    const float s = key_score(key);
+    st.lo = fminf(st.lo, s);
+    st.hi = fmaxf(st.hi, s);
   }
-  st.cnt[0] += n0;
-  st.cnt[1] += n1;
+  st.cnt += __popcll(m);
+}
+
+__device__ __forceinline__ void emit_key(u64 x, int pos, int kk, int32_t* oi, float* os) {
+  if (pos < kk) {                                     // exactly kk pass; the bound only guards the row
+    oi[pos] = key_index(x);
+    if (os) os[pos] = key_score(x);
+  }
 }
 
 // Emit the exact top-kk of buf[0..cnt) (all of it when cnt <= kk) to one
 // output row of kk entries, then pad with -1 / -inf.
-__device__ void wave_emit(const u64* buf, int cnt, int kk, uint32_t* hist, int32_t* oi, float* os) {
+__device__ __forceinline__ void wave_emit(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi, float* os) {
   const int l = lane_id();
-  u64 T = 0ull;
-  if (cnt > kk) T = wave_select_kth(buf, cnt, kk, hist);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
   int w = 0;
-  for (int base = 0; base < cnt; base += WAVE) {
-    const int i = base + l;
-    const u64 x = i < cnt ? buf[i] : 0ull;
-    const bool keep = i < cnt && x >= T;
+  const u64 T = st.cnt > kk ? wave_select_kth_stream(st.cand, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  wave_stream(st.cand, st.cnt, [&](u64 v, int) {
+    const bool keep = v >= T;                          // T >= 1 excludes slots past the end
     const u64 m = ballot(keep);
-    const int pos = w + lanes_below(m);
-    if (keep && pos < kk) {                           // exactly kk pass; the bound only guards the row
-      oi[pos] = key_index(x);
-      if (os) os[pos] = key_score(x);
-    }
+    if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
     w += __popcll(m);
-  }
+  });
   w = w < kk ? w : kk;
   for (int i = w + l; i < kk; i += WAVE) {
     oi[i] = -1;
     if (os) os[i] = -__builtin_inff();
   }
-}
-
-// Rows whose visible keys all fit (vis <= kk) and whose scores are not asked
-// for: the selection is every visible key.
-__device__ void wave_emit_all_visible(int vis, int part, int P, int kk, int32_t* oi) {
-  const int l = lane_id();
-  for (int i = l; i < kk; i += WAVE) oi[i] = i < vis ? part + P * i : -1;
 }
 
 __device__ __forceinline__ void decode_item(const PrefillArgs& a, int it, int& b, int& qb, int& part) {
@@ -135,24 +124,10 @@ __device__ __forceinline__ int round_item(int r) {
   return r * G + ((r & 1) ? (G - 1 - (int)blockIdx.x) : (int)blockIdx.x);
 }
 
+// Does any row of the block need scores (more visible keys than kk, scores
+// requested, or threshold mode)?  Also the block's largest visible count.
 template <int MODE>
-__device__ void finish_rows(const PrefillArgs& a, SlotPair& st, int b, int r0, int part,
-                            uint32_t* hist) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int row = r0 + s;
-    if (row >= a.S_q) continue;
-    const size_t orow = (size_t)b * a.S_q + row;
-    int32_t* oi = a.out_idx + orow * a.out_stride + (size_t)part * a.kk;
-    float* os = a.out_score ? a.out_score + orow * a.out_stride + (size_t)part * a.kk : nullptr;
-    wave_emit(st.cand[s], st.cnt[s], a.kk, hist, oi, os);
-    if (MODE == MODE_THRESHOLD && lane_id() == 0) a.out_count[orow] = st.surv[s];
-  }
-}
-
-template <int MODE>
-__device__ __forceinline__ bool block_needs_scores(const PrefillArgs& a, int b, int qb, int part,
-                                                   int& vis_max) {
+__device__ __forceinline__ bool block_needs_scores(const PrefillArgs& a, int b, int qb, int part, int& vis_max) {
   vis_max = 0;
   bool need = MODE == MODE_THRESHOLD || a.need_scores;
   for (int r = 0; r < PF_ROWS; ++r) {
@@ -163,28 +138,71 @@ __device__ __forceinline__ bool block_needs_scores(const PrefillArgs& a, int b, 
   return need;
 }
 
-// ============================================================ MFMA prefill
-//
-// bf16, H = 64 heads, D = 128.  One wave multiplies its 2 queries x 64 heads
-// (4 row tiles of 32 heads, held as MFMA A operands in registers) with 32-key
-// column tiles read from LDS: v_mfma_f32_32x32x16_bf16, fp32 accumulation,
-// 8 steps over D.  Output lane l holds key column (l & 31) and 16 heads of a
-// row tile; ReLU and the head weights are applied in registers, the two lane
-// halves are summed, and each lane ends with one (slot, key) score.
+__device__ __forceinline__ int32_t* out_row(const PrefillArgs& a, int b, int row, int part) {
+  return a.out_idx + ((size_t)b * a.S_q + row) * a.out_stride + (size_t)part * a.kk;
+}
 
-constexpr int MH = 64, MD = 128;
-constexpr int KROW = MD + 8;   // LDS row pitch in bf16 (272 B): conflict-free 16-B reads
+// A row whose visible keys all fit (vis <= kk) and whose scores are not asked
+// for: the selection is every visible key.
+__device__ __forceinline__ void wave_emit_all_visible(const PrefillArgs& a, int b, int row, int part, int vis) {
+  const int l = lane_id();
+  int32_t* oi = out_row(a, b, row, part);
+  for (int i = l; i < a.kk; i += WAVE) oi[i] = i < vis ? part + a.P * i : -1;
+}
 
 template <int MODE>
-__global__ __launch_bounds__(PF_THREADS) void prefill_mfma_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 ktile[2][PF_KTILE * KROW];
-  __shared__ float wsh[PF_ROWS][MH];
+__device__ __forceinline__ void finish_row(const PrefillArgs& a, Slot& st, int b, int row, int part, uint32_t* hist, u64* list) {
+  if (row >= a.S_q) return;
+  const size_t orow = (size_t)b * a.S_q + row;
+  float* os = a.out_score ? a.out_score + orow * a.out_stride + (size_t)part * a.kk : nullptr;
+  wave_emit(st, a.kk, hist, list, out_row(a, b, row, part), os);
+  if (MODE == MODE_THRESHOLD && lane_id() == 0) a.out_count[orow] = st.surv;
+}
+
+__device__ __forceinline__ void slot_init(Slot& st, const PrefillArgs& a, int wv, int mode) {
+  st.cand = a.cand + ((size_t)blockIdx.x * PF_ROWS + wv) * a.C;
+  st.cnt = 0;
+  st.thr = mode == MODE_THRESHOLD ? a.thr_fixed : 0ull;
+  st.surv = 0;
+  st.lo = __builtin_inff();
+  st.hi = -__builtin_inff();
+}
+
+// ============================================================ MFMA prefill
+//
+// bf16, H = 64 heads, D = 128.  A wave holds its query's 64 heads x 128 as
+// MFMA A operands (2 row tiles of 32 heads, 64 VGPRs) and its 64 head weights
+// in registers, and per step multiplies them with two 32-key column tiles read
+// from LDS: v_mfma_f32_32x32x16_bf16, fp32 accumulation, 8 k-steps over D.
+// Output lane l holds key column (l & 31) and 16 heads of a row tile; ReLU and
+// the head weights are applied in registers; exchanging the two column tiles'
+// half-wave partial sums leaves lanes 0-31 with the scores of tile 0 and lanes
+// 32-63 with those of tile 1.  Two workgroups share a CU (two waves per SIMD),
+// so one wave's VALU epilogue overlaps the other's MFMAs.
+
+constexpr int MH = 64, MD = 128;
+// A key tile (PF_KTILE keys x 256 B) sits in LDS as groups of 16 keys; inside
+// a group the 16-byte d-chunks are plane-major:
+//     byte(key, chunk) = (key / 16) * 4096 + chunk * 256 + (key % 16) * 16.
+// A wave's direct-to-LDS load (global_load_lds_dwordx4) fills 1 KB contiguous
+// = 16 keys x 4 chunks (64 B of each key row), and the MFMA B-operand read
+// (32 keys x one chunk per half-wave) hits 16 distinct bank quads per 16
+// lanes, with the k-step in the instruction's immediate offset.
+constexpr int KT_BYTES = PF_KTILE * MD * 2;
+
+template <int MODE>
+__global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ktile[2][KT_BYTES];
   __shared__ uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
+  __shared__ u64 list_all[PF_THREADS / WAVE][WAVE_LIST];
 
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   uint32_t* hist = hist_all[wv];
+  u64* list = list_all[wv];
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
+  // B-operand read offset of this lane inside a stage (column tile 0, k-step 0)
+  const int b_off = ((l >> 4) & 1) * 4096 + (l >> 5) * 256 + (l & 15) * 16;
 
   for (int r = 0;; ++r) {
     const int it = round_item(r);
@@ -194,119 +212,108 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_mfma_kernel(PrefillArgs a)
     decode_item(a, it, b, qb, part);
     int vis_max;
     const bool need = block_needs_scores<MODE>(a, b, qb, part, vis_max);
-    const int r0 = qb * PF_ROWS + 2 * wv;             // this wave's two rows
-    const int vis0 = row_visible(a, b, r0, part), vis1 = row_visible(a, b, r0 + 1, part);
+    const int row = qb * PF_ROWS + wv;                // this wave's query row
+    const int vis = row_visible(a, b, row, part);
     if (!need) {
-      for (int s = 0; s < 2; ++s) {
-        const int row = r0 + s;
-        if (row >= a.S_q) continue;
-        const size_t orow = (size_t)b * a.S_q + row;
-        wave_emit_all_visible(s ? vis1 : vis0, part, a.P, a.kk,
-                              a.out_idx + orow * a.out_stride + (size_t)part * a.kk);
-      }
+      if (row < a.S_q) wave_emit_all_visible(a, b, row, part, vis);
       continue;
     }
 
-    __syncthreads();                                  // LDS of the previous item is free
-    for (int e = tid; e < PF_ROWS * MH; e += PF_THREADS) {
-      const int rr = e / MH, h = e % MH, row = qb * PF_ROWS + rr;
-      wsh[rr][h] = row < a.S_q ? a.w[((size_t)b * a.S_q + row) * MH + h] : 0.f;
+    bf16x8 A[2][8];
+    float wl[2][16];
+    const int rq = row < a.S_q ? row : a.S_q - 1;     // rows past the end compute on a valid row, emit nothing
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const bf16x8* src = (const bf16x8*)(Q + (((size_t)b * a.S_q + rq) * MH + rt * 32 + (l & 31)) * MD);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
+      const float* wrow = a.w + ((size_t)b * a.S_q + rq) * MH + rt * 32 + 4 * (l >> 5);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wl[rt][i] = wrow[8 * (i >> 2) + (i & 3)];
     }
-    bf16x8 A[4][8];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int row = r0 + (rt >> 1);
-      if (row < a.S_q) {
-        const bf16x8* src = (const bf16x8*)(Q + (((size_t)b * a.S_q + row) * MH + (rt & 1) * 32 + (l & 31)) * MD);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) A[rt][kk] = bf16x8{};
-      }
-    }
-    SlotPair st;
-    st.cand[0] = a.cand + ((size_t)blockIdx.x * PF_ROWS + 2 * wv) * a.C;
-    st.cand[1] = st.cand[0] + a.C;
-    st.cnt[0] = st.cnt[1] = 0;
-    st.thr[0] = st.thr[1] = (MODE == MODE_THRESHOLD) ? a.thr_fixed : 0ull;
-    st.surv[0] = st.surv[1] = 0;
+    Slot st;
+    slot_init(st, a, wv, MODE);
 
     const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
-    // stage loader: 64 rows x 16 chunks of 16 B; 4 chunks per thread
-    u32x4 stage[4];
-    auto load_tile = [&](int t) {
+    const size_t kseq = (size_t)b * a.T;
+    // direct-to-LDS stage load: this wave fills blocks wv, wv+4, wv+8, wv+12 (1 KB each)
+    auto load_tile = [&](int t, int buf) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int c = tid + e * PF_THREADS, row = c >> 4, col = c & 15;
-        const int j = t * PF_KTILE + row;
-        if (j < vis_max) {
-          const size_t s = (size_t)part + (size_t)a.P * j;
-          stage[e] = *(const u32x4*)(K + ((size_t)b * a.T + s) * MD + col * 8);
-        } else {
-          stage[e] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const int blk = e * 4 + wv, grp = blk >> 2, quad = blk & 3;
+        int j = t * PF_KTILE + grp * 16 + (l & 15);
+        j = j < vis_max ? j : vis_max - 1;            // rows past the end: any valid row (masked later)
+        const int chunk = quad * 4 + (l >> 4);
+        const __bf16* src = K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, (void*)&ktile[buf][blk * 1024], 16, 0, 0);
       }
     };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = tid + e * PF_THREADS, row = c >> 4, col = c & 15;
-        *(u32x4*)(&ktile[buf][row * KROW + col * 8]) = stage[e];
-      }
-    };
-    if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
-    }
+    // Step t covers keys [64t, 64t+64): column tile 0 = keys 64t + (l & 31),
+    // column tile 1 = keys 64t + 32 + (l & 31).  The MFMAs of one column tile
+    // run interleaved with the ReLU/weight epilogue of the previous one:
+    //   phase 1 of step t:  MFMA(tile 1 of t)   || epilogue(tile 0 of t)
+    //   barrier            (stage t+1 has landed, stage t is no longer read)
+    //   phase 2 of step t:  MFMA(tile 0 of t+1) || epilogue(tile 1 of t), offer
+    __syncthreads();                                  // previous item's readers are done with the stages
+    if (ntiles > 0) load_tile(0, 0);
     __syncthreads();
 
+    // Step t covers keys [64t, 64t+64): column tile 0 = keys 64t + (l & 31),
+    // column tile 1 = keys 64t + 32 + (l & 31).
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1);
+      if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+      const char* kb = &ktile[buf][b_off];
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[c][rt] = f32x16{};
+      // B operands one k-step ahead; the scheduling fences keep the compiler
+      // from hoisting all 16 LDS reads (64 VGPRs) to the top of the step.
+      bf16x8 b0 = *(const bf16x8*)(kb);
+      bf16x8 b1 = *(const bf16x8*)(kb + 8192);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        bf16x8 n0 = b0, n1 = b1;
+        if (kk + 1 < 8) {
+          n0 = *(const bf16x8*)(kb + (kk + 1) * 512);
+          n1 = *(const bf16x8*)(kb + 8192 + (kk + 1) * 512);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          acc[0][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], b0, acc[0][rt], 0, 0, 0);
+          acc[1][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], b1, acc[1][rt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        b0 = n0;
+        b1 = n1;
+      }
+      float part2[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        f32x16 acc[4];
+        float ps = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x16{};
-        const __bf16* kb = &ktile[buf][(c * 32 + (l & 31)) * KROW + 8 * (l >> 5)];
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 bfr = *(const bf16x8*)(kb + 16 * kk);
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-            acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], bfr, acc[rt], 0, 0, 0);
-        }
-        float part0 = 0.f, part1 = 0.f;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const float* wr = &wsh[2 * wv + (rt >> 1)][(rt & 1) * 32 + 4 * (l >> 5)];
-          float ps = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = acc[rt][i];
-            ps = __builtin_fmaf(wr[8 * (i >> 2) + (i & 3)], x > 0.f ? x : 0.f, ps);
-          }
-          if (rt >> 1) part1 += ps; else part0 += ps;
-        }
-        const float o0 = __shfl_xor(part0, 32, WAVE);
-        const float o1 = __shfl_xor(part1, 32, WAVE);
-        const float score = (l < 32) ? part0 + o0 : part1 + o1;
-        const int j = t * PF_KTILE + c * 32 + (l & 31);
-        const bool valid = j < ((l < 32) ? vis0 : vis1);
-        const u64 key = make_key(score, (uint32_t)(part + a.P * j));
-        wave_offer<MODE>(st, key, valid, a, hist);
+          for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[c][rt][i]), ps);
+        part2[c] = ps;
       }
-      if (t + 1 < ntiles) store_tile(buf ^ 1);
-      __syncthreads();
+      // lanes 0-31 take tile 0's keys, lanes 32-63 tile 1's: swap the other half's partial sums
+      const float o0 = __shfl_xor(part2[0], 32, WAVE);
+      const float o1 = __shfl_xor(part2[1], 32, WAVE);
+      const float score = (l < 32) ? part2[0] + o0 : part2[1] + o1;
+      const int j = t * PF_KTILE + l;
+      wave_offer<MODE>(st, score, (uint32_t)(part + a.P * j), j < vis, a, hist, list);
+      __syncthreads();                                 // stage t+1 landed (vmcnt 0) and stage t is free
     }
-    finish_rows<MODE>(a, st, b, r0, part, hist);
+    finish_row<MODE>(a, st, b, row, part, hist, list);
   }
 }
 
 // ============================================================ generic prefill
 //
-// Any H, D and dtype (fp32 or bf16): each lane computes one (slot, key)
+// Any H, D and dtype (fp32 or bf16): each lane computes one (query, key)
 // score with fp32 FMAs in index order (exact for small-integer inputs).  No
 // workgroup barriers: waves are independent.
 
@@ -320,8 +327,10 @@ __device__ __forceinline__ float ld_f32<__bf16>(const __bf16* p, size_t i) { ret
 template <int MODE, typename Tin>
 __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs a) {
   __shared__ uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
+  __shared__ u64 list_all[PF_THREADS / WAVE][WAVE_LIST];
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   uint32_t* hist = hist_all[wv];
+  u64* list = list_all[wv];
   const Tin* Q = (const Tin*)a.q;
   const Tin* K = (const Tin*)a.k;
 
@@ -333,33 +342,19 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs
     decode_item(a, it, b, qb, part);
     int vis_max;
     const bool need = block_needs_scores<MODE>(a, b, qb, part, vis_max);
-    const int r0 = qb * PF_ROWS + 2 * wv;
-    const int vis0 = row_visible(a, b, r0, part), vis1 = row_visible(a, b, r0 + 1, part);
+    const int row = qb * PF_ROWS + wv;
+    const int vis = row_visible(a, b, row, part);
+    if (row >= a.S_q) continue;
     if (!need) {
-      for (int s = 0; s < 2; ++s) {
-        const int row = r0 + s;
-        if (row >= a.S_q) continue;
-        const size_t orow = (size_t)b * a.S_q + row;
-        wave_emit_all_visible(s ? vis1 : vis0, part, a.P, a.kk,
-                              a.out_idx + orow * a.out_stride + (size_t)part * a.kk);
-      }
+      wave_emit_all_visible(a, b, row, part, vis);
       continue;
     }
-    SlotPair st;
-    st.cand[0] = a.cand + ((size_t)blockIdx.x * PF_ROWS + 2 * wv) * a.C;
-    st.cand[1] = st.cand[0] + a.C;
-    st.cnt[0] = st.cnt[1] = 0;
-    st.thr[0] = st.thr[1] = (MODE == MODE_THRESHOLD) ? a.thr_fixed : 0ull;
-    st.surv[0] = st.surv[1] = 0;
-
-    const int slot = l >> 5;
-    const int row = r0 + slot;
-    const int vis_me = slot ? vis1 : vis0;
-    const int vmax = vis0 > vis1 ? vis0 : vis1;
-    const size_t qoff = ((size_t)b * a.S_q + (row < a.S_q ? row : 0)) * a.H;
-    for (int j0 = 0; j0 < vmax; j0 += 32) {
-      const int j = j0 + (l & 31);
-      const bool valid = j < vis_me;
+    Slot st;
+    slot_init(st, a, wv, MODE);
+    const size_t qoff = ((size_t)b * a.S_q + row) * a.H;
+    for (int j0 = 0; j0 < vis; j0 += WAVE) {
+      const int j = j0 + l;
+      const bool valid = j < vis;
       float score = 0.f;
       uint32_t s_idx = 0;
       if (valid) {
@@ -369,12 +364,12 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs
           float dot = 0.f;
           const size_t qh = (qoff + h) * a.D;
           for (int d = 0; d < a.D; ++d) dot = __builtin_fmaf(ld_f32(Q, qh + d), ld_f32(K, koff + d), dot);
-          score = __builtin_fmaf(a.w[qoff + h], dot > 0.f ? dot : 0.f, score);
+          score = __builtin_fmaf(a.w[qoff + h], relu(dot), score);
         }
       }
-      wave_offer<MODE>(st, make_key(score, s_idx), valid, a, hist);
+      wave_offer<MODE>(st, score, s_idx, valid, a, hist, list);
     }
-    finish_rows<MODE>(a, st, b, r0, part, hist);
+    finish_row<MODE>(a, st, b, row, part, hist, list);
   }
 }
 
@@ -444,10 +439,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_score_kernel(DecodeArgs a)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float x = acc[rt][e];
-          ps = __builtin_fmaf(wl[rt][e], x > 0.f ? x : 0.f, ps);
-        }
+        for (int e = 0; e < 16; ++e) ps = __builtin_fmaf(wl[rt][e], relu(acc[rt][e]), ps);
       part[c] = ps;
     }
     const float o0 = __shfl_xor(part[0], 32, WAVE);
@@ -459,44 +451,59 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_score_kernel(DecodeArgs a)
 }
 
 // decode_select: one workgroup per query row; exact top-kk of the row's
-// dense scores, emitted in index order of a deterministic block scan.
+// dense scores, emitted in element order through a deterministic block scan.
+constexpr int DEC_REG = 32;                              // keys per thread: rows up to 32768 in registers
+
+__device__ __forceinline__ void block_emit_step(bool keep, u64 x, int& w, int kk, int* wcnt, int32_t* oi,
+                                                float* os) {
+  constexpr int NW = DEC_SEL_THREADS / WAVE;
+  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  const u64 m = ballot(keep);
+  if (l == 0) wcnt[wv] = __popcll(m);
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int j = 0; j < NW; ++j) {
+    off += j < wv ? wcnt[j] : 0;
+    tot += wcnt[j];
+  }
+  if (keep) emit_key(x, w + off + lanes_below(m), kk, oi, os);
+  w += tot;
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeArgs a) {
   __shared__ uint32_t hist[SEL_BINS];
   __shared__ u64 red[2 * DEC_SEL_THREADS / WAVE];
+  __shared__ u64 list[BLOCK_LIST];
   __shared__ int wcnt[DEC_SEL_THREADS / WAVE];
-  constexpr int NW = DEC_SEL_THREADS / WAVE;
-  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  __shared__ int lcnt;
+  const int tid = threadIdx.x;
   const int row = blockIdx.x, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
   const float* sc = a.scores + (size_t)row * a.T;
   int32_t* oi = a.out_idx + (size_t)row * a.kk;
   float* os = a.out_score ? a.out_score + (size_t)row * a.kk : nullptr;
-  u64 T = 0ull;
-  if (vis > a.kk) T = block_select_kth_dense<DEC_SEL_THREADS>(sc, vis, a.kk, hist, red);
   int w = 0;
-  for (int base = 0; base < vis; base += DEC_SEL_THREADS) {
-    const int s = base + tid;
-    u64 x = 0ull;
-    bool keep = false;
-    if (s < vis) {
-      x = make_key(sc[s], (uint32_t)s);
-      keep = x >= T;
+  if (vis <= DEC_REG * DEC_SEL_THREADS) {
+    u64 x[DEC_REG];
+#pragma unroll
+    for (int j = 0; j < DEC_REG; ++j) {
+      const int s = j * DEC_SEL_THREADS + tid;
+      const float v = sc[s < vis ? s : (vis > 0 ? vis - 1 : 0)];
+      x[j] = s < vis ? make_key(v, (uint32_t)s) : 0ull;
     }
-    const u64 m = ballot(keep);
-    if (l == 0) wcnt[wv] = __popcll(m);
-    __syncthreads();
-    int off = 0, tot = 0;
-    for (int j = 0; j < NW; ++j) {
-      off += j < wv ? wcnt[j] : 0;
-      tot += wcnt[j];
+    const u64 T = vis > a.kk ? block_select_kth_regs<DEC_SEL_THREADS, DEC_REG>(x, vis, a.kk, hist, red, list, &lcnt) : 1ull;
+#pragma unroll
+    for (int j = 0; j < DEC_REG; ++j) {
+      if (j * DEC_SEL_THREADS < vis) block_emit_step(x[j] >= T, x[j], w, a.kk, wcnt, oi, os);
     }
-    const int pos = w + off + lanes_below(m);
-    if (keep && pos < a.kk) {
-      oi[pos] = s;
-      if (os) os[pos] = key_score(x);
+  } else {
+    const u64 T = block_select_kth_dense<DEC_SEL_THREADS>(sc, vis, a.kk, hist, red);
+    for (int base = 0; base < vis; base += DEC_SEL_THREADS) {
+      const int s = base + tid;
+      const u64 x = s < vis ? make_key(sc[s], (uint32_t)s) : 0ull;
+      block_emit_step(s < vis && x >= T, x, w, a.kk, wcnt, oi, os);
     }
-    w += tot;
-    __syncthreads();
   }
   w = w < a.kk ? w : a.kk;
   for (int e = w + tid; e < a.kk; e += DEC_SEL_THREADS) {
