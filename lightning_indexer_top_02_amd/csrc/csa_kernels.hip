@@ -24,6 +24,15 @@ namespace csa {
 // negative as int32, non-negative ones keep their order; -0.0 becomes +0.0.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Two column tiles' per-lane partial sums (each lane holds half of its key's
+// heads; lane l and lane l^32 hold the two halves): returns, in lanes 0-31,
+// the full score of tile 0's key (l & 31) and, in lanes 32-63, tile 1's.
+// v_permlane32_swap moves tile 0's upper half down and tile 1's lower half up.
+__device__ __forceinline__ float half_swap_sum(float p0, float p1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int row_visible(const PrefillArgs& a, int b, int row, int part) {
   if (row >= a.S_q) return 0;
   long long v = a.causal ? (a.q_pos0 + row) / a.m + 1 : (long long)a.T;
@@ -37,18 +46,36 @@ __device__ __forceinline__ int row_visible(const PrefillArgs& a, int b, int row,
   return (int)v;
 }
 
-// Top-k state of the wave's query row (wave-uniform except lo/hi).
+// Top-k state of the wave's query row (wave-uniform except lo/hi).  The
+// append threshold is kept as a (score, index) pair: a key (s, i) may enter
+// iff s > thr_s, or s == thr_s and i <= thr_i -- the same total order as the
+// 64-bit keys, with float compares (-0.0 == +0.0).
 struct Slot {
   u64* cand;     // candidate buffer (C keys)
   int cnt;       // keys in it
-  u64 thr;       // keys below thr cannot enter the top-k
+  float thr_s;   // append threshold (inclusive on the index)
+  uint32_t thr_i;
   int surv;      // threshold mode: keys >= thr_fixed seen
   float lo, hi;  // per lane: bounds on the scores this lane appended
 };
 
-// Keep the exact top-kk of buf[0..cnt) in place (cnt > kk); returns the new
-// append threshold (one above the kk-th key).  Streams the buffer: the
-// wave's MFMA operands stay in registers meanwhile.
+// Inclusive key bound X (keys >= X pass) as a (score, index) threshold.
+__device__ __forceinline__ void key_to_thr(u64 X, float& ts, uint32_t& ti) {
+  if (X == 0ull) {                                    // everything passes
+    ts = -__builtin_inff();
+    ti = 0xFFFFFFFFu;
+  } else {
+    ts = key_score(X);
+    ti = 0xFFFFFFFFu - (uint32_t)X;
+  }
+}
+
+__device__ __forceinline__ bool passes(float s, uint32_t i, float ts, uint32_t ti) {
+  return s > ts || (s == ts && i <= ti);
+}
+
+// Keep the exact top-kk of buf[0..cnt) in place (cnt > kk); returns the kk-th
+// key.  Streams the buffer: the wave's MFMA operands stay in registers meanwhile.
 __device__ __forceinline__ u64 wave_compact(u64* buf, int cnt, int kk, uint32_t* hist, u64* list, float lo,
                                            float hi) {
   const u64 T = wave_select_kth_stream(buf, cnt, kk, hist, list, lo, hi);
@@ -59,28 +86,33 @@ __device__ __forceinline__ u64 wave_compact(u64* buf, int cnt, int kk, uint32_t*
     if (keep) buf[w + lanes_below(m)] = v;
     w += __popcll(m);
   });
-  return T + 1ull;
+  return T;
 }
 
-// Offer one key per lane (valid lanes only) to the wave's query.
+// Offer one (score, index) per lane (valid lanes only) to the wave's query.
 template <int MODE>
 __device__ __forceinline__ void wave_offer(Slot& st, float score, uint32_t idx, bool valid, const PrefillArgs& a,
                                            uint32_t* hist, u64* list) {
   if (st.cnt + WAVE > a.C) {                          // make room: at most 64 appends per offer
-    const u64 t = wave_compact(st.cand, st.cnt, a.kk, hist, list, st.lo, st.hi);
-    st.thr = t > st.thr ? t : st.thr;
+    const u64 T = wave_compact(st.cand, st.cnt, a.kk, hist, list, st.lo, st.hi);
     st.cnt = a.kk;
-    st.lo = key_score(t - 1ull);                       // every survivor scores >= the kk-th
+    st.lo = key_score(T);                              // every survivor scores >= the kk-th
+    // new keys must beat the kk-th key T (and, in threshold mode, still pass thr_fixed)
+    const u64 X = (MODE == MODE_THRESHOLD && a.thr_fixed > T + 1ull) ? a.thr_fixed : T + 1ull;
+    key_to_thr(X, st.thr_s, st.thr_i);
   }
-  const u64 key = make_key(score, idx);
-  if (MODE == MODE_THRESHOLD) st.surv += __popcll(ballot(valid && key >= a.thr_fixed));
-  const bool keep = valid && key >= st.thr;
+  if (MODE == MODE_THRESHOLD) {
+    float fs;
+    uint32_t fi;
+    key_to_thr(a.thr_fixed, fs, fi);
+    st.surv += __popcll(ballot(valid && passes(score, idx, fs, fi)));
+  }
+  const bool keep = valid && passes(score, idx, st.thr_s, st.thr_i);
   const u64 m = ballot(keep);
   if (keep) {
-    st.cand[st.cnt + lanes_below(m)] = key;
-    const float s = key_score(key);
-    st.lo = fminf(st.lo, s);
-    st.hi = fmaxf(st.hi, s);
+    st.cand[st.cnt + lanes_below(m)] = make_key(score, idx);
+    st.lo = fminf(st.lo, score);
+    st.hi = fmaxf(st.hi, score);
   }
   st.cnt += __popcll(m);
 }
@@ -162,7 +194,7 @@ __device__ __forceinline__ void finish_row(const PrefillArgs& a, Slot& st, int b
 __device__ __forceinline__ void slot_init(Slot& st, const PrefillArgs& a, int wv, int mode) {
   st.cand = a.cand + ((size_t)blockIdx.x * PF_ROWS + wv) * a.C;
   st.cnt = 0;
-  st.thr = mode == MODE_THRESHOLD ? a.thr_fixed : 0ull;
+  key_to_thr(mode == MODE_THRESHOLD ? a.thr_fixed : 0ull, st.thr_s, st.thr_i);
   st.surv = 0;
   st.lo = __builtin_inff();
   st.hi = -__builtin_inff();
@@ -203,6 +235,14 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
   const __bf16* K = (const __bf16*)a.k;
   // B-operand read offset of this lane inside a stage (column tile 0, k-step 0)
   const int b_off = ((l >> 4) & 1) * 4096 + (l >> 5) * 256 + (l & 15) * 16;
+  // byte offsets of this lane's 16-B pieces in the wave's four stage blocks,
+  // relative to the tile's first key row (rows are P keys apart)
+  uint32_t doff[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int blk = e * 4 + wv, row = (blk >> 2) * 16 + (l & 15), chunk = (blk & 3) * 4 + (l >> 4);
+    doff[e] = (uint32_t)(((size_t)row * a.P * MD + chunk * 8) * 2);
+  }
 
   for (int r = 0;; ++r) {
     const int it = round_item(r);
@@ -236,24 +276,29 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
 
     const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
     const size_t kseq = (size_t)b * a.T;
-    // direct-to-LDS stage load: this wave fills blocks wv, wv+4, wv+8, wv+12 (1 KB each)
+    // direct-to-LDS stage load: this wave fills blocks wv, wv+4, wv+8, wv+12 (1 KB
+    // each); a tile whose 64 rows all lie below T takes one uniform base plus the
+    // wave's constant lane offsets, a tile crossing T clamps its rows.
     auto load_tile = [&](int t, int buf) {
+      const size_t row0 = kseq + (size_t)part + (size_t)a.P * (size_t)(t * PF_KTILE);
+      if ((long long)part + (long long)a.P * (t * PF_KTILE + PF_KTILE - 1) < a.T) {
+        const char* base = (const char*)(K + row0 * MD);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int blk = e * 4 + wv, grp = blk >> 2, quad = blk & 3;
-        int j = t * PF_KTILE + grp * 16 + (l & 15);
-        j = j < vis_max ? j : vis_max - 1;            // rows past the end: any valid row (masked later)
-        const int chunk = quad * 4 + (l >> 4);
-        const __bf16* src = K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8;
-        __builtin_amdgcn_global_load_lds((const void*)src, (void*)&ktile[buf][blk * 1024], 16, 0, 0);
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_global_load_lds((const void*)(base + doff[e]), (void*)&ktile[buf][(e * 4 + wv) * 1024], 16,
+                                           0, 0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int blk = e * 4 + wv, grp = blk >> 2, quad = blk & 3;
+          int j = t * PF_KTILE + grp * 16 + (l & 15);
+          j = j < vis_max ? j : vis_max - 1;          // rows past the end: any valid row (masked later)
+          const int chunk = quad * 4 + (l >> 4);
+          const __bf16* src = K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8;
+          __builtin_amdgcn_global_load_lds((const void*)src, (void*)&ktile[buf][blk * 1024], 16, 0, 0);
+        }
       }
     };
-    // Step t covers keys [64t, 64t+64): column tile 0 = keys 64t + (l & 31),
-    // column tile 1 = keys 64t + 32 + (l & 31).  The MFMAs of one column tile
-    // run interleaved with the ReLU/weight epilogue of the previous one:
-    //   phase 1 of step t:  MFMA(tile 1 of t)   || epilogue(tile 0 of t)
-    //   barrier            (stage t+1 has landed, stage t is no longer read)
-    //   phase 2 of step t:  MFMA(tile 0 of t+1) || epilogue(tile 1 of t), offer
     __syncthreads();                                  // previous item's readers are done with the stages
     if (ntiles > 0) load_tile(0, 0);
     __syncthreads();
@@ -299,10 +344,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
           for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[c][rt][i]), ps);
         part2[c] = ps;
       }
-      // lanes 0-31 take tile 0's keys, lanes 32-63 tile 1's: swap the other half's partial sums
-      const float o0 = __shfl_xor(part2[0], 32, WAVE);
-      const float o1 = __shfl_xor(part2[1], 32, WAVE);
-      const float score = (l < 32) ? part2[0] + o0 : part2[1] + o1;
+      const float score = half_swap_sum(part2[0], part2[1]);
       const int j = t * PF_KTILE + l;
       wave_offer<MODE>(st, score, (uint32_t)(part + a.P * j), j < vis, a, hist, list);
       __syncthreads();                                 // stage t+1 landed (vmcnt 0) and stage t is free
@@ -442,9 +484,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_score_kernel(DecodeArgs a)
         for (int e = 0; e < 16; ++e) ps = __builtin_fmaf(wl[rt][e], relu(acc[rt][e]), ps);
       part[c] = ps;
     }
-    const float o0 = __shfl_xor(part[0], 32, WAVE);
-    const float o1 = __shfl_xor(part[1], 32, WAVE);
-    const float score = (l < 32) ? part[0] + o0 : part[1] + o1;
+    const float score = half_swap_sum(part[0], part[1]);
     const int s = base + l;                 // lanes 0-31: column tile 0, lanes 32-63: tile 1
     if (s < end) out[s] = score;
   }
