@@ -114,19 +114,14 @@ PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, ui
 bool decode_fast(const csa_problem* p) { return use_mfma(p) && p->S_q <= CSA_MAX_DECODE_SQ; }
 
 struct DecodePlan {
-  int chunk, nsplit;
+  int nsplit;
   size_t score_bytes, sort_bytes, total;
 };
 
 DecodePlan plan_decode(const csa_problem* p, int kk, uint32_t flags) {
   DecodePlan d;
-  d.chunk = 1024;
-  if (const char* e = std::getenv("CSA_DECODE_CHUNK")) {
-    int v = std::atoi(e);
-    if (v >= 256) d.chunk = (v + 255) / 256 * 256;
-  }
-  d.nsplit = (p->T + d.chunk - 1) / d.chunk;
-  d.score_bytes = align_up((size_t)p->B * p->S_q * p->T * sizeof(float));
+  d.nsplit = (p->T + csa::DEC_CHUNK - 1) / csa::DEC_CHUNK;
+  d.score_bytes = align_up((size_t)p->B * p->S_q * (p->T + csa::DEC_PAD) * sizeof(float));
   d.sort_bytes = (flags & CSA_SORTED) ? align_up((size_t)p->B * p->S_q * kk * sizeof(float)) : 0;
   d.total = d.score_bytes + d.sort_bytes;
   return d;
@@ -275,7 +270,6 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
     a.B = prob->B; a.S_q = prob->S_q; a.T = prob->T; a.m = prob->m; a.q_pos0 = prob->q_pos0;
     a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
     a.scores = (float*)ws;
-    a.chunk = d.chunk;
     a.kk = topk;
     a.out_idx = out_idx;
     a.out_score = score_dst;

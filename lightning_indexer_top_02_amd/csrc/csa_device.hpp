@@ -357,8 +357,8 @@ __device__ __forceinline__ u64 wave_select_kth_stream(const u64* buf, int n, int
   return wave_radix_kth(y, w, r, hist, AnyKey{});
 }
 
-// Block versions for the decode select: NT threads, R keys per thread
-// (x[j] = key of element j*NT + tid).  hist: SEL_BINS entries; red: >= 2*NT/WAVE
+// Block versions for the decode select: NT threads, R keys per thread in any
+// element layout (0 marks an empty slot).  hist: SEL_BINS entries; red: >= 2*NT/WAVE
 // u64; list: BLOCK_LIST u64; cnt: one int of LDS.
 template <int NT, int R, typename Pred>
 __device__ __forceinline__ u64 block_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* red, Pred in) {
@@ -369,7 +369,7 @@ __device__ __forceinline__ u64 block_radix_kth(const u64 (&x)[R], int n, int k, 
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const u64 v = x[j];
-    if (j * NT < n && in(v)) {
+    if (in(v)) {
       lo = v < lo ? v : lo;
       hi = v > hi ? v : hi;
     }
@@ -398,11 +398,9 @@ __device__ __forceinline__ u64 block_radix_kth(const u64 (&x)[R], int n, int k, 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      if (j * NT < n) {
-        const u64 v = x[j];
-        const bool match = in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix);
-        if (match) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
-      }
+      const u64 v = x[j];
+      const bool match = in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix);
+      if (match) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (wv == 0) {
@@ -428,7 +426,7 @@ __device__ __forceinline__ u64 block_select_kth_regs(const u64 (&x)[R], int n, i
   float slo = __builtin_inff(), shi = -__builtin_inff();
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    if (j * NT < n && x[j]) {
+    if (x[j]) {
       const float s = key_score(x[j]);
       slo = fminf(slo, s);
       shi = fmaxf(shi, s);
@@ -453,7 +451,7 @@ __device__ __forceinline__ u64 block_select_kth_regs(const u64 (&x)[R], int n, i
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    if (j * NT < n && x[j]) atomicAdd(&hist[lb(x[j])], 1u);
+    if (x[j]) atomicAdd(&hist[lb(x[j])], 1u);
   }
   __syncthreads();
   if (wv == 0) {
@@ -467,7 +465,7 @@ __device__ __forceinline__ u64 block_select_kth_regs(const u64 (&x)[R], int n, i
   if (bcnt > BLOCK_LIST) return block_radix_kth<NT>(x, n, r, hist, red, inb);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    if (j * NT < n && inb(x[j])) list[atomicAdd(cnt, 1)] = x[j];   // order within the bin is irrelevant
+    if (inb(x[j])) list[atomicAdd(cnt, 1)] = x[j];   // order within the bin is irrelevant
   }
   __syncthreads();
   if (wv == 0) {

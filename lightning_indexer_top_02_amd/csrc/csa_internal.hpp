@@ -49,14 +49,15 @@ struct DecodeArgs {
   int B, S_q, T, m;
   long long q_pos0;
   int causal;
-  float* scores;        // [B*S_q][T] fp32 workspace
-  int chunk;            // keys per workgroup along T (multiple of 256)
+  float* scores;        // [B*S_q][T + DEC_PAD] fp32 workspace
   int kk;
   int32_t* out_idx;
   float* out_score;
 };
 
 constexpr int DEC_THREADS = 256;
+constexpr int DEC_CHUNK = 1024;        // keys per decode-scan workgroup
+constexpr int DEC_PAD = 64;            // floats after each score row (stores of keys past the end)
 constexpr int DEC_SEL_THREADS = 1024;
 
 // mfma: the bf16 H=64 D=128 MFMA kernel; otherwise the generic kernel for a.bf16.

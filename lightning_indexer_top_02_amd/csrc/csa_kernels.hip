@@ -433,83 +433,82 @@ __device__ __forceinline__ int decode_visible(const DecodeArgs& a, int b, int i)
   return (int)v;
 }
 
-__global__ __launch_bounds__(DEC_THREADS) void decode_score_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.y, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
-  const int start = blockIdx.x * a.chunk;
-  const int end = start + a.chunk < vis ? start + a.chunk : vis;
+  const int start = blockIdx.x * DEC_CHUNK;
+  const int end = start + DEC_CHUNK < vis ? start + DEC_CHUNK : vis;
   if (start >= end) return;
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
 
   bf16x8 A[2][8];
+  float wl[2][16];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const bf16x8* src = (const bf16x8*)(Q + ((size_t)row * MH + rt * 32 + (l & 31)) * MD);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wl[rt][e] = a.w[(size_t)row * MH + rt * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3)];
   }
-  float wl[2][16];
+  // Each wave takes 32-key steps round-robin; the next step's key rows are
+  // requested before the current step's MFMAs so ~8 KB per wave is in flight.
+  float* out = a.scores + (size_t)row * (a.T + DEC_PAD);
+  const size_t kseq = (size_t)b * a.T;
+  constexpr int STEP = 32, STRIDE = STEP * (DEC_THREADS / WAVE);
+  auto load = [&](int base, bf16x8 (&bf)[8]) {
+    int s = base + (l & 31);
+    s = s < end ? s : end - 1;
+    const bf16x8* src = (const bf16x8*)(K + (kseq + s) * MD);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int kk = 0; kk < 8; ++kk) bf[kk] = src[2 * kk + (l >> 5)];
+  };
+  // one step on the key rows in `cur` while the next step's rows load into `nxt`
+  auto step = [&](int base, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) -> float {
+    load(base + STRIDE, nxt);                         // unconditional: rows past `end` are clamped
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      wl[rt][e] = a.w[(size_t)row * MH + rt * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3)];
-
-  float* out = a.scores + (size_t)row * a.T;
-  for (int base = start + 64 * wv; base < end; base += 64 * (DEC_THREADS / WAVE)) {
-    bf16x8 Bf[2][8];
+    for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      int s = base + 32 * c + (l & 31);
-      s = s < end ? s : end - 1;
-      const bf16x8* src = (const bf16x8*)(K + ((size_t)b * a.T + s) * MD);
+      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], cur[kk], acc[rt], 0, 0, 0);
+    float ps = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) Bf[c][kk] = src[2 * kk + (l >> 5)];
-    }
-    float part[2];
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f32x16 acc[2] = {f32x16{}, f32x16{}};
+      for (int e = 0; e < 16; ++e) ps = __builtin_fmaf(wl[rt][e], relu(acc[rt][e]), ps);
+    return half_swap_sum(ps, ps);                     // both halves: the full score of key (l & 31)
+  };
+  // The chunk is a compile-time DEC_CHUNK keys (DEC_CHUNK / STRIDE steps per
+  // wave), so the step loop unrolls completely: ping-pong buffers without
+  // register copies and exact wait counts for the prefetched rows.
+  // Scores stay in registers until the loop ends: with only loads inside it,
+  // the compiler's wait counts for the prefetched rows are exact.
+  static_assert(DEC_CHUNK % STRIDE == 0, "decode chunk must be whole steps");
+  constexpr int NSTEP = DEC_CHUNK / STRIDE;
+  bf16x8 b0[8], b1[8];
+  float sc[NSTEP];
+  const int base0 = start + STEP * wv;
+  load(base0, b0);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
+  for (int st = 0; st < NSTEP; st += 2) {
+    sc[st] = step(base0 + st * STRIDE, b0, b1);
+    if (st + 1 < NSTEP) sc[st + 1] = step(base0 + (st + 1) * STRIDE, b1, b0);
+  }
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], Bf[c][kk], acc[rt], 0, 0, 0);
-      float ps = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ps = __builtin_fmaf(wl[rt][e], relu(acc[rt][e]), ps);
-      part[c] = ps;
-    }
-    const float score = half_swap_sum(part[0], part[1]);
-    const int s = base + l;                 // lanes 0-31: column tile 0, lanes 32-63: tile 1
-    if (s < end) out[s] = score;
+  for (int st = 0; st < NSTEP; ++st) {               // no branch: keys past the end go to the row's pad
+    const int s = base0 + st * STRIDE + (l & 31);
+    out[s < end ? s : a.T + (l & 31)] = sc[st];       // lanes l and l^32 store the same value
   }
 }
 
 // decode_select: one workgroup per query row; exact top-kk of the row's
-// dense scores, emitted in element order through a deterministic block scan.
-constexpr int DEC_REG = 32;                              // keys per thread: rows up to 32768 in registers
-
-__device__ __forceinline__ void block_emit_step(bool keep, u64 x, int& w, int kk, int* wcnt, int32_t* oi,
-                                                float* os) {
-  constexpr int NW = DEC_SEL_THREADS / WAVE;
-  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
-  const u64 m = ballot(keep);
-  if (l == 0) wcnt[wv] = __popcll(m);
-  __syncthreads();
-  int off = 0, tot = 0;
-  for (int j = 0; j < NW; ++j) {
-    off += j < wv ? wcnt[j] : 0;
-    tot += wcnt[j];
-  }
-  if (keep) emit_key(x, w + off + lanes_below(m), kk, oi, os);
-  w += tot;
-  __syncthreads();
-}
+// dense scores.  Wave w holds the contiguous element range [w*2048, w*2048+2048)
+// in registers (element w*2048 + j*64 + lane in x[j]), so the emit needs one
+// exchange of per-wave counts and keeps element order (deterministic output).
+constexpr int DEC_REG = 32;                              // keys per lane: rows up to 32768 in registers
 
 __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeArgs a) {
   __shared__ uint32_t hist[SEL_BINS];
@@ -517,32 +516,60 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
   __shared__ u64 list[BLOCK_LIST];
   __shared__ int wcnt[DEC_SEL_THREADS / WAVE];
   __shared__ int lcnt;
-  const int tid = threadIdx.x;
+  constexpr int NW = DEC_SEL_THREADS / WAVE;
+  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.x, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
-  const float* sc = a.scores + (size_t)row * a.T;
+  const float* sc = a.scores + (size_t)row * (a.T + DEC_PAD);
   int32_t* oi = a.out_idx + (size_t)row * a.kk;
   float* os = a.out_score ? a.out_score + (size_t)row * a.kk : nullptr;
   int w = 0;
   if (vis <= DEC_REG * DEC_SEL_THREADS) {
     u64 x[DEC_REG];
+    const int e0 = wv * (DEC_REG * WAVE) + l;
 #pragma unroll
     for (int j = 0; j < DEC_REG; ++j) {
-      const int s = j * DEC_SEL_THREADS + tid;
+      const int s = e0 + j * WAVE;
       const float v = sc[s < vis ? s : (vis > 0 ? vis - 1 : 0)];
       x[j] = s < vis ? make_key(v, (uint32_t)s) : 0ull;
     }
-    const u64 T = vis > a.kk ? block_select_kth_regs<DEC_SEL_THREADS, DEC_REG>(x, vis, a.kk, hist, red, list, &lcnt) : 1ull;
+    const u64 T = vis > a.kk ? block_select_kth_regs<DEC_SEL_THREADS, DEC_REG>(x, vis, a.kk, hist, red, list, &lcnt)
+                             : 1ull;
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(x[j] >= T));
+    if (l == 0) wcnt[wv] = mine;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int j = 0; j < NW; ++j) {
+      off += j < wv ? wcnt[j] : 0;
+      tot += wcnt[j];
+    }
 #pragma unroll
     for (int j = 0; j < DEC_REG; ++j) {
-      if (j * DEC_SEL_THREADS < vis) block_emit_step(x[j] >= T, x[j], w, a.kk, wcnt, oi, os);
+      const bool keep = x[j] >= T;
+      const u64 m = ballot(keep);
+      if (keep) emit_key(x[j], off + lanes_below(m), a.kk, oi, os);
+      off += __popcll(m);
     }
+    w = tot;
   } else {
     const u64 T = block_select_kth_dense<DEC_SEL_THREADS>(sc, vis, a.kk, hist, red);
     for (int base = 0; base < vis; base += DEC_SEL_THREADS) {
       const int s = base + tid;
       const u64 x = s < vis ? make_key(sc[s], (uint32_t)s) : 0ull;
-      block_emit_step(s < vis && x >= T, x, w, a.kk, wcnt, oi, os);
+      const bool keep = s < vis && x >= T;
+      const u64 m = ballot(keep);
+      if (l == 0) wcnt[wv] = __popcll(m);
+      __syncthreads();
+      int off = 0, tot = 0;
+      for (int j = 0; j < NW; ++j) {
+        off += j < wv ? wcnt[j] : 0;
+        tot += wcnt[j];
+      }
+      if (keep) emit_key(x, w + off + lanes_below(m), a.kk, oi, os);
+      w += tot;
+      __syncthreads();
     }
   }
   w = w < a.kk ? w : a.kk;
