@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -206,6 +208,16 @@ def main():
         sys.exit(1)
     L.load_library()
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
     if args.only_decode:
         print(json.dumps(bench_decode(args, torch, L, csa_inputs, R)), flush=True)
         return
