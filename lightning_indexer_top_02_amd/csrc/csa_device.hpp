@@ -58,6 +58,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Order this wave's earlier global stores before its later global loads of
+// the same addresses.  A workgroup-scope fence lowers to no wait at all here,
+// and a load issued while a store to its address is still in flight can
+// return the old contents; draining the vector memory counter (vmcnt = 0,
+// other counters untouched) completes the stores first.
+__device__ __forceinline__ void wave_own_stores_visible() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0) expcnt(7) lgkmcnt(15)
+  asm volatile("" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_bcast(T v, int src) {
   return __shfl(v, src, WAVE);
@@ -117,40 +127,73 @@ struct BinPick {
   int count;  // keys in it
 };
 
-// Given a histogram of `nb` bins (nb <= SEL_BINS) in LDS, find the bin that
-// holds rank `rank` counted from the top.  Whole wave calls it; result is
-// uniform.  Bins are scanned from the highest down.
+// Given a histogram of `nb` bins (nb <= SEL_BINS, a power of two, 16-byte
+// aligned) in LDS, find the bin that holds rank `rank` counted from the top.
+// Whole wave calls it; result is uniform.  Two levels: lane l sums its run of
+// nb/64 bins (lane 0 the highest run) with 16-byte reads, a scan finds the run
+// holding the rank, then one bin of that run per lane and a second scan find
+// the bin.  Inconsistent counts (no run or bin holds the rank) give count 0.
 __device__ __forceinline__ BinPick wave_pick_bin(const uint32_t* hist, int nb, int rank) {
   const int l = lane_id();
   const int per = nb >= WAVE ? nb / WAVE : 1;
-  const int hi_bin = nb - 1 - l * per;            // this lane covers bins hi_bin .. hi_bin-per+1
+  const int lo_bin = nb - (l + 1) * per;          // this lane's run: lo_bin .. lo_bin + per - 1
   int s = 0;
-  if (hi_bin >= 0) {
-    for (int j = 0; j < per; ++j) s += (int)hist[hi_bin - j];
+  if (lo_bin >= 0) {
+    if ((per & 3) == 0) {
+      for (int j = 0; j < per; j += 4) {
+        const uint4 h = *(const uint4*)&hist[lo_bin + j];
+        s += (int)(h.x + h.y + h.z + h.w);
+      }
+    } else {
+      for (int j = 0; j < per; ++j) s += (int)hist[lo_bin + j];
+    }
   }
   const int incl = wave_incl_scan(s);
   const int excl = incl - s;
-  const bool mine = hi_bin >= 0 && excl < rank && rank <= incl;
-  const u64 who = ballot(mine);
-  const int src = who ? (int)__builtin_ctzll(who) : 0;   // no lane: inconsistent counts, caller stops
-  int bin = 0, above = 0, cnt = 0;
-  if (mine) {
-    int cum = excl;
-    for (int j = 0; j < per; ++j) {
-      const int b = hi_bin - j;
-      const int h = (int)hist[b];
-      if (cum + h >= rank) {
-        bin = b; above = cum; cnt = h;
-        break;
-      }
-      cum += h;
-    }
-  }
-  BinPick r;
-  r.bin = wave_bcast(bin, src);
-  r.above = wave_bcast(above, src);
-  r.count = wave_bcast(cnt, src);
+  const u64 who = ballot(lo_bin >= 0 && excl < rank && rank <= incl);
+  BinPick r{0, 0, 0};
+  if (!who) return r;
+  const int src = (int)__builtin_ctzll(who);
+  const int top = nb - 1 - src * per;             // highest bin of the chosen run
+  const int above = __builtin_amdgcn_readlane(excl, src);
+  const int h = l < per ? (int)hist[top - l] : 0; // lane i: bin top - i
+  const int incl2 = above + wave_incl_scan(h);
+  const u64 hit = ballot(l < per && incl2 - h < rank && rank <= incl2);
+  if (!hit) return r;
+  const int s2 = (int)__builtin_ctzll(hit);
+  r.bin = top - s2;
+  r.count = __builtin_amdgcn_readlane(h, s2);
+  r.above = __builtin_amdgcn_readlane(incl2, s2) - r.count;
   return r;
+}
+
+// Zero hist[0..nb) (16-byte aligned) with 16-byte stores where nb allows.
+__device__ __forceinline__ void wave_clear_hist(uint32_t* hist, int nb) {
+  const int l = lane_id();
+  if (nb >= 4 * WAVE) {
+    for (int b = 4 * l; b < nb; b += 4 * WAVE) *(uint4*)&hist[b] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    for (int b = l; b < nb; b += WAVE) hist[b] = 0u;
+  }
+}
+
+// The r-th largest of w distinct keys list[0..w) (1 <= r <= w <= WAVE): the
+// key with exactly r - 1 keys above it, found by comparing every pair (each
+// lane holds one key and compares it with all others via readlane).
+__device__ __forceinline__ u64 wave_small_kth(const u64* list, int w, int r) {
+  const int l = lane_id();
+  const u64 v = l < w ? list[l] : 0ull;
+  const uint32_t vh = (uint32_t)(v >> 32), vl = (uint32_t)v;
+  int g = 0;
+  for (int s = 0; s < w; ++s) {
+    const u64 o = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)vh, s) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((int)vl, s);
+    g += o > v ? 1 : 0;
+  }
+  const u64 m = ballot(l < w && g == r - 1);
+  const int src = m ? (int)__builtin_ctzll(m) : 0;
+  return ((u64)(uint32_t)__builtin_amdgcn_readlane((int)vh, src) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)vl, src);
 }
 
 // ---------------------------------------------------------------- register-resident select
@@ -230,7 +273,7 @@ __device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, u
     const int shift = hi_bit - rb;
     const int nb = 1 << rb;
     const uint32_t dmask = (uint32_t)(nb - 1);
-    for (int b = l; b < nb; b += WAVE) hist[b] = 0u;
+    wave_clear_hist(hist, nb);
     wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -250,6 +293,56 @@ __device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, u
   }
 }
 
+// Exact k-th largest of the n keys held in x (n > k >= 1): linear-bin
+// histogram, gather of the bin holding rank k into `list`, radix resolution;
+// the same steps as the streaming version below without any memory pass.
+// slo/shi: per-lane bounds on the scores in x (+inf/-inf where a lane has none).
+template <int R>
+__device__ __forceinline__ u64 wave_select_kth_regs(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* list,
+                                                    float slo, float shi) {
+  const int l = lane_id();
+  slo = wave_min_f32(slo);
+  shi = wave_max_f32(shi);
+  LinBins lb;
+  if (!lin_bins_ok(slo, shi, lb)) return wave_radix_kth(x, n, k, hist, AnyKey{});
+  wave_clear_hist(hist, SEL_BINS);
+  wave_lds_sync();
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if (j * WAVE < n && x[j]) atomicAdd(&hist[lb(x[j])], 1u);
+  wave_lds_sync();
+  const BinPick pk = wave_pick_bin(hist, SEL_BINS, k);
+  wave_lds_sync();
+  const int r = k - pk.above;
+  const InBin inb{lb, pk.bin};
+  if (pk.count > WAVE_LIST) return wave_radix_kth(x, n, r, hist, inb);
+  int w = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const bool in = j * WAVE < n && inb(x[j]);
+    const u64 m = ballot(in);
+    if (in) list[w + lanes_below(m)] = x[j];
+    w += __popcll(m);
+  }
+  wave_lds_sync();
+  if (w <= WAVE) return wave_small_kth(list, w, r);
+  constexpr int RL = WAVE_LIST / WAVE;
+  u64 y[RL];
+#pragma unroll
+  for (int j = 0; j < RL; ++j) {
+    const int i = j * WAVE + l;
+    y[j] = i < w ? list[i] : 0ull;
+  }
+  wave_lds_sync();
+  if (w == r) {
+    u64 mn = ~0ull;
+#pragma unroll
+    for (int j = 0; j < RL; ++j) mn = (y[j] && y[j] < mn) ? y[j] : mn;
+    return wave_min_u64(mn);
+  }
+  return wave_radix_kth(y, w, r, hist, AnyKey{});
+}
+
 // ---------------------------------------------------------------- streaming select
 //
 // The same selection over keys in global memory written earlier by this
@@ -266,7 +359,7 @@ __device__ __forceinline__ void wave_stream(const u64* buf, int n, F f) {
 #pragma unroll
     for (int j = 0; j < STREAM_BATCH; ++j) {
       const int i = base + j * WAVE + l;
-      v[j] = i < n ? buf[i] : 0ull;
+      v[j] = i < n ? __builtin_nontemporal_load(&buf[i]) : 0ull;   // candidate buffers stream past L2
     }
 #pragma unroll
     for (int j = 0; j < STREAM_BATCH; ++j) f(v[j], base + j * WAVE);   // 0 = past the end
@@ -294,7 +387,7 @@ __device__ __forceinline__ u64 wave_radix_kth_stream(const u64* buf, int n, int 
     const int shift = hi_bit - rb;
     const int nb = 1 << rb;
     const uint32_t dmask = (uint32_t)(nb - 1);
-    for (int b = l; b < nb; b += WAVE) hist[b] = 0u;
+    wave_clear_hist(hist, nb);
     wave_lds_sync();
     wave_stream(buf, n, [&](u64 v, int) {
       if (in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix)) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
@@ -316,12 +409,12 @@ __device__ __forceinline__ u64 wave_radix_kth_stream(const u64* buf, int n, int 
 __device__ __forceinline__ u64 wave_select_kth_stream(const u64* buf, int n, int k, uint32_t* hist, u64* list,
                                                       float slo, float shi) {
   const int l = lane_id();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");   // this wave's global stores -> its loads (same CU)
+  wave_own_stores_visible();
   slo = wave_min_f32(slo);
   shi = wave_max_f32(shi);
   LinBins lb;
   if (!lin_bins_ok(slo, shi, lb)) return wave_radix_kth_stream(buf, n, k, hist, AnyKey{});
-  for (int b = l; b < SEL_BINS; b += WAVE) hist[b] = 0u;
+  wave_clear_hist(hist, SEL_BINS);
   wave_lds_sync();
   wave_stream(buf, n, [&](u64 v, int) {
     if (v) atomicAdd(&hist[lb(v)], 1u);
@@ -340,6 +433,7 @@ __device__ __forceinline__ u64 wave_select_kth_stream(const u64* buf, int n, int
     w += __popcll(m);
   });
   wave_lds_sync();
+  if (w <= WAVE) return wave_small_kth(list, w, r);
   constexpr int RL = WAVE_LIST / WAVE;
   u64 y[RL];
 #pragma unroll
@@ -477,7 +571,9 @@ __device__ __forceinline__ u64 block_select_kth_regs(const u64 (&x)[R], int n, i
       y[j] = i < bcnt ? list[i] : 0ull;
     }
     u64 T;
-    if (bcnt == r) {
+    if (bcnt <= WAVE) {
+      T = wave_small_kth(list, bcnt, r);
+    } else if (bcnt == r) {
       u64 mn = ~0ull;
 #pragma unroll
       for (int j = 0; j < RL; ++j) mn = (y[j] && y[j] < mn) ? y[j] : mn;

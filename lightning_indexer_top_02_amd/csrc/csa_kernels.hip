@@ -59,6 +59,11 @@ struct Slot {
   float lo, hi;  // per lane: bounds on the scores this lane appended
 };
 
+// Candidate buffers and output rows are written once and read at most once
+// more by the same wave: their loads and stores are non-temporal, so that
+// they stream past L2 instead of evicting the key tiles every workgroup
+// re-reads there.
+
 // Inclusive key bound X (keys >= X pass) as a (score, index) threshold.
 __device__ __forceinline__ void key_to_thr(u64 X, float& ts, uint32_t& ti) {
   if (X == 0ull) {                                    // everything passes
@@ -83,7 +88,7 @@ __device__ __forceinline__ u64 wave_compact(u64* buf, int cnt, int kk, uint32_t*
   wave_stream(buf, cnt, [&](u64 v, int) {        // in order; writes never pass the reads
     const bool keep = v >= T && v != 0ull;
     const u64 m = ballot(keep);
-    if (keep) buf[w + lanes_below(m)] = v;
+    if (keep) __builtin_nontemporal_store(v, &buf[w + lanes_below(m)]);
     w += __popcll(m);
   });
   return T;
@@ -110,7 +115,7 @@ __device__ __forceinline__ void wave_offer(Slot& st, float score, uint32_t idx, 
   const bool keep = valid && passes(score, idx, st.thr_s, st.thr_i);
   const u64 m = ballot(keep);
   if (keep) {
-    st.cand[st.cnt + lanes_below(m)] = make_key(score, idx);
+    __builtin_nontemporal_store(make_key(score, idx), &st.cand[st.cnt + lanes_below(m)]);
     st.lo = fminf(st.lo, score);
     st.hi = fmaxf(st.hi, score);
   }
@@ -119,24 +124,47 @@ __device__ __forceinline__ void wave_offer(Slot& st, float score, uint32_t idx, 
 
 __device__ __forceinline__ void emit_key(u64 x, int pos, int kk, int32_t* oi, float* os) {
   if (pos < kk) {                                     // exactly kk pass; the bound only guards the row
-    oi[pos] = key_index(x);
-    if (os) os[pos] = key_score(x);
+    __builtin_nontemporal_store(key_index(x), &oi[pos]);
+    if (os) __builtin_nontemporal_store(key_score(x), &os[pos]);
   }
 }
+
+// Candidate buffers up to this size are selected from registers at the end
+// of a row: one load pass with every load in flight instead of three
+// latency-bound streaming passes (the MFMA operands are dead by then).
+constexpr int EMIT_REGS = 66;
 
 // Emit the exact top-kk of buf[0..cnt) (all of it when cnt <= kk) to one
 // output row of kk entries, then pad with -1 / -inf.
 __device__ __forceinline__ void wave_emit(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi, float* os) {
   const int l = lane_id();
   int w = 0;
-  const u64 T = st.cnt > kk ? wave_select_kth_stream(st.cand, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  wave_stream(st.cand, st.cnt, [&](u64 v, int) {
-    const bool keep = v >= T;                          // T >= 1 excludes slots past the end
-    const u64 m = ballot(keep);
-    if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
-    w += __popcll(m);
-  });
+  if (st.cnt <= EMIT_REGS * WAVE) {
+    wave_own_stores_visible();
+    u64 x[EMIT_REGS];
+#pragma unroll
+    for (int j = 0; j < EMIT_REGS; ++j) {
+      const int i = j * WAVE + l;
+      x[j] = i < st.cnt ? __builtin_nontemporal_load(&st.cand[i]) : 0ull;
+    }
+    const u64 T = st.cnt > kk ? wave_select_kth_regs(x, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
+#pragma unroll
+    for (int j = 0; j < EMIT_REGS; ++j) {
+      const bool keep = x[j] >= T;                     // T >= 1 excludes empty slots
+      const u64 m = ballot(keep);
+      if (keep) emit_key(x[j], w + lanes_below(m), kk, oi, os);
+      w += __popcll(m);
+    }
+  } else {
+    const u64 T = st.cnt > kk ? wave_select_kth_stream(st.cand, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
+    wave_own_stores_visible();
+    wave_stream(st.cand, st.cnt, [&](u64 v, int) {
+      const bool keep = v >= T;                        // T >= 1 excludes slots past the end
+      const u64 m = ballot(keep);
+      if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
+      w += __popcll(m);
+    });
+  }
   w = w < kk ? w : kk;
   for (int i = w + l; i < kk; i += WAVE) {
     oi[i] = -1;
@@ -179,7 +207,7 @@ __device__ __forceinline__ int32_t* out_row(const PrefillArgs& a, int b, int row
 __device__ __forceinline__ void wave_emit_all_visible(const PrefillArgs& a, int b, int row, int part, int vis) {
   const int l = lane_id();
   int32_t* oi = out_row(a, b, row, part);
-  for (int i = l; i < a.kk; i += WAVE) oi[i] = i < vis ? part + a.P * i : -1;
+  for (int i = l; i < a.kk; i += WAVE) __builtin_nontemporal_store(i < vis ? part + a.P * i : -1, &oi[i]);
 }
 
 template <int MODE>
@@ -198,6 +226,62 @@ __device__ __forceinline__ void slot_init(Slot& st, const PrefillArgs& a, int wv
   st.surv = 0;
   st.lo = __builtin_inff();
   st.hi = -__builtin_inff();
+}
+
+// ============================================================ LDS staging helpers
+
+constexpr int WS_SPIN_LIMIT = 1 << 22;          // bounded spins: about 0.3 s before giving up
+
+__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }   // compiler-only barrier
+// Empty register constraint: the value must exist in a VGPR at this point of the schedule.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ int lds_load(int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
+// One add per wave (lane 0): executed by every lane it would count 64 times.
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  if (lane_id() == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Wait until *ctr >= target; false if the workgroup aborted (or this wait ran out).
+__device__ __forceinline__ bool spin_ge(int* ctr, int target, int* abort) {
+  int n = 0;
+  while (lds_load(ctr) < target) {
+    if (lds_load(abort)) return false;
+    if (++n > WS_SPIN_LIMIT) {
+      lds_store(abort, 1);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  mem_order();
+  return true;
+}
+
+// s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l
+// (lds is the same in every lane).
+// Written as asm so that the compiler does not treat every later LDS access
+// as a possible reader of the in-flight load (it would drain vmcnt to 0 before
+// each one); the caller orders the data with explicit vmcnt waits instead.
+// The instruction has no register results (only its address operand, read at
+// issue), and this kernel holds nothing else in M0 (only these sequences
+// write it), so clobbering M0 here is safe.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform LDS base
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
 
 // ============================================================ MFMA prefill
@@ -225,7 +309,7 @@ constexpr int KT_BYTES = PF_KTILE * MD * 2;
 template <int MODE>
 __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char ktile[2][KT_BYTES];
-  __shared__ uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
   __shared__ u64 list_all[PF_THREADS / WAVE][WAVE_LIST];
 
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
@@ -285,8 +369,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
         const char* base = (const char*)(K + row0 * MD);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_global_load_lds((const void*)(base + doff[e]), (void*)&ktile[buf][(e * 4 + wv) * 1024], 16,
-                                           0, 0);
+          dma16(base + doff[e], lds_addr(&ktile[buf][(e * 4 + wv) * 1024]));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -295,12 +378,15 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
           j = j < vis_max ? j : vis_max - 1;          // rows past the end: any valid row (masked later)
           const int chunk = quad * 4 + (l >> 4);
           const __bf16* src = K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8;
-          __builtin_amdgcn_global_load_lds((const void*)src, (void*)&ktile[buf][blk * 1024], 16, 0, 0);
+          dma16(src, lds_addr(&ktile[buf][blk * 1024]));
         }
       }
     };
     __syncthreads();                                  // previous item's readers are done with the stages
     if (ntiles > 0) load_tile(0, 0);
+    // tile 0 and the query loads have landed; the compiler, which does not see
+    // the tile loads, then has no load of its own pending inside the loop
+    wait_vmcnt<0>();
     __syncthreads();
 
     // Step t covers keys [64t, 64t+64): column tile 0 = keys 64t + (l & 31),
@@ -347,9 +433,238 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
       const float score = half_swap_sum(part2[0], part2[1]);
       const int j = t * PF_KTILE + l;
       wave_offer<MODE>(st, score, (uint32_t)(part + a.P * j), j < vis, a, hist, list);
-      __syncthreads();                                 // stage t+1 landed (vmcnt 0) and stage t is free
+      wait_vmcnt<0>();                                 // this wave's part of tile t+1 landed
+      __syncthreads();                                 // all of tile t+1 landed and stage t is free
     }
     finish_row<MODE>(a, st, b, row, part, hist, list);
+  }
+}
+
+// ============================================================ wave-specialised MFMA prefill
+//
+// Same scores and selection as prefill_mfma_kernel, with the work split by
+// role inside a workgroup of 8 waves (one workgroup per CU):
+//   waves 0-3  "score waves": MFMA + ReLU/weights for query row j = wave; they
+//              push each 64-key tile of scores into an LDS ring and never
+//              touch global memory after loading their query;
+//   waves 4-7  "select waves": for row j = wave-4 they pop score tiles, filter
+//              and append candidates, compact, and run the final select while
+//              the score waves already work on the next query block.
+// No s_barrier inside the loop.  Key tiles rotate through WS_NS LDS stages;
+// the score waves coordinate them with per-stage LDS counters (loads landed,
+// reads done), and each score/select pair shares the ring's produced and
+// consumed counters.  Every wait is a bounded spin; a spin that runs out sets
+// an abort flag that ends all waves of the workgroup.
+
+constexpr int WS_THREADS = 512;
+constexpr int WS_NS = 4;                      // key-tile stages (tiles t+1..t+3 in flight at step t)
+constexpr int WS_RING = 32;                   // score tiles buffered per row
+
+struct WsSync {
+  int kfill[WS_NS];  // per stage: completed (wave, tile) loads
+  int kfree[WS_NS];  // per stage: completed (wave, tile) reads
+  int prod[PF_ROWS]; // per row: score tiles pushed
+  int cons[PF_ROWS]; // per row: score tiles popped
+  int abort;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(WS_THREADS, 1) void prefill_ws_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kst[WS_NS][KT_BYTES];
+  __shared__ float ring[PF_ROWS][WS_RING][WAVE];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[PF_ROWS][SEL_BINS];
+  __shared__ u64 list_all[PF_ROWS][WAVE_LIST];
+  __shared__ WsSync sy;
+
+  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  if (tid < (int)(sizeof(WsSync) / sizeof(int))) ((int*)&sy)[tid] = 0;
+  __syncthreads();
+
+  if (wv < PF_ROWS) {
+    // ------------------------------------------------------------ score wave
+    const int j = wv;
+    const __bf16* Q = (const __bf16*)a.q;
+    const __bf16* K = (const __bf16*)a.k;
+    const int b_off = ((l >> 4) & 1) * 4096 + (l >> 5) * 256 + (l & 15) * 16;
+    const uint32_t kst_lds = lds_addr(&kst[0][0]);
+    uint32_t doff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int blk = e * 4 + j, row = (blk >> 2) * 16 + (l & 15), chunk = (blk & 3) * 4 + (l >> 4);
+      doff[e] = (uint32_t)(((size_t)row * a.P * MD + chunk * 8) * 2);
+    }
+    int gt = 0;                                       // key tiles loaded so far (same in all score waves)
+    int prod = 0;                                     // score tiles pushed for row j
+    for (int r = 0;; ++r) {
+      const int it = round_item(r);
+      if (r * (int)gridDim.x >= a.n_items) break;
+      if (it >= a.n_items) continue;
+      int b, qb, part;
+      decode_item(a, it, b, qb, part);
+      int vis_max;
+      if (!block_needs_scores<MODE>(a, b, qb, part, vis_max)) continue;
+      const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
+      if (ntiles == 0) continue;
+      const int row = qb * PF_ROWS + j;
+      const int rq = row < a.S_q ? row : a.S_q - 1;
+      bf16x8 A[2][8];
+      float wl[2][16];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const bf16x8* src = (const bf16x8*)(Q + (((size_t)b * a.S_q + rq) * MH + rt * 32 + (l & 31)) * MD);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
+        const float* wrow = a.w + ((size_t)b * a.S_q + rq) * MH + rt * 32 + 4 * (l >> 5);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wl[rt][i] = wrow[8 * (i >> 2) + (i & 3)];
+      }
+      // Drain the query loads here: the compiler knows nothing of the key-tile
+      // loads below, and a query load it still counted as pending would make it
+      // wait inside the tile loop for every load in flight.
+      wait_vmcnt<0>();
+      const size_t kseq = (size_t)b * a.T;
+      const int n0 = gt;                              // tile t of this item is global tile n0 + t
+      // tile t -> stage (n0 + t) % WS_NS, its use number in that stage (n0 + t) / WS_NS
+      auto fill = [&](int t) -> bool {                // wait for the stage to be free, then load tile t
+        const int n = n0 + t, s = n % WS_NS;
+        if (!spin_ge(&sy.kfree[s], PF_ROWS * (n / WS_NS), &sy.abort)) return false;
+        const uint32_t lds = kst_lds + s * KT_BYTES + j * 1024;
+        const size_t row0 = kseq + (size_t)part + (size_t)a.P * (size_t)(t * PF_KTILE);
+        if ((long long)part + (long long)a.P * (t * PF_KTILE + PF_KTILE - 1) < a.T) {
+          const char* base = (const char*)(K + row0 * MD);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dma16(base + doff[e], lds + e * 4096);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int blk = e * 4 + j, grp = blk >> 2, quad = blk & 3;
+            int jj = t * PF_KTILE + grp * 16 + (l & 15);
+            jj = jj < vis_max ? jj : vis_max - 1;
+            const int chunk = quad * 4 + (l >> 4);
+            dma16(K + (kseq + (size_t)part + (size_t)a.P * jj) * MD + chunk * 8, lds + e * 4096);
+          }
+        }
+        return true;
+      };
+      // tile t has landed for this wave once at most `later` newer tiles are in flight
+      auto publish = [&](int t, int later) -> bool {
+        if (later >= 2) wait_vmcnt<8>();
+        else if (later == 1) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+        mem_order();
+        const int n = n0 + t, s = n % WS_NS;
+        lds_add(&sy.kfill[s], 1);
+        return spin_ge(&sy.kfill[s], PF_ROWS * (n / WS_NS + 1), &sy.abort);
+      };
+      auto stage = [&](int t) { return (const char*)&kst[(n0 + t) % WS_NS][0] + b_off; };
+      f32x16 acc0[2], acc1[2];
+      auto mma = [&](const char* kb, f32x16 (&acc)[2]) {
+        acc[0] = f32x16{};
+        acc[1] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 bb = *(const bf16x8*)(kb + kk * 512);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0][kk], bb, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1][kk], bb, acc[1], 0, 0, 0);
+        }
+      };
+      auto epi = [&](const f32x16 (&acc)[2]) {
+        float ps = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[rt][i]), ps);
+        return ps;
+      };
+      // epilogue of the previous half tile interleaved with the MFMAs of the next
+      auto phase = [&](const char* kb, f32x16 (&acc_new)[2], const f32x16 (&acc_old)[2]) {
+        float ps = epi(acc_old);
+        mma(kb, acc_new);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        pin(ps);
+        return ps;
+      };
+      bool ok = true;
+      const int pre = ntiles < WS_NS - 1 ? ntiles : WS_NS - 1;
+      for (int t = 0; ok && t < pre; ++t) ok = fill(t);
+      if (ok) ok = publish(0, pre - 1);
+      if (ok) mma(stage(0), acc0);
+      for (int t = 0; ok && t < ntiles; ++t) {
+        const float p0 = phase(stage(t) + 8192, acc1, acc0);   // second half of tile t
+        __builtin_amdgcn_sched_barrier(0);
+        mem_order();
+        lds_add(&sy.kfree[(n0 + t) % WS_NS], 1);              // done reading tile t
+        float p1;
+        if (t + 1 < ntiles) {
+          if (t + WS_NS - 1 < ntiles && !(ok = fill(t + WS_NS - 1))) break;
+          const int last = t + WS_NS - 1 < ntiles - 1 ? t + WS_NS - 1 : ntiles - 1;
+          if (!(ok = publish(t + 1, last - (t + 1)))) break;
+          __builtin_amdgcn_sched_barrier(0);
+          p1 = phase(stage(t + 1), acc0, acc1);                 // first half of tile t+1
+        } else {
+          p1 = epi(acc1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const float score = half_swap_sum(p0, p1);
+        // push the tile of 64 scores to the select wave of row j
+        if (!(ok = spin_ge(&sy.cons[j], prod + 1 - WS_RING, &sy.abort))) break;
+        ring[j][prod % WS_RING][l] = score;
+        mem_order();
+        ++prod;
+        lds_store(&sy.prod[j], prod);
+      }
+      gt += ntiles;
+      if (!ok) {
+        wait_vmcnt<0>();                              // no load left in flight at exit
+        break;
+      }
+    }
+  } else {
+    // ------------------------------------------------------------ select wave
+    const int j = wv - PF_ROWS;
+    uint32_t* hist = hist_all[j];
+    u64* list = list_all[j];
+    int cons = 0;
+    for (int r = 0;; ++r) {
+      const int it = round_item(r);
+      if (r * (int)gridDim.x >= a.n_items) break;
+      if (it >= a.n_items) continue;
+      int b, qb, part;
+      decode_item(a, it, b, qb, part);
+      int vis_max;
+      const bool need = block_needs_scores<MODE>(a, b, qb, part, vis_max);
+      const int row = qb * PF_ROWS + j;
+      const int vis = row_visible(a, b, row, part);
+      if (!need) {
+        if (row < a.S_q) wave_emit_all_visible(a, b, row, part, vis);
+        continue;
+      }
+      const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
+      Slot st;
+      slot_init(st, a, j, MODE);
+      bool ok = true;
+      for (int t = 0; t < ntiles; ++t) {
+        if (!spin_ge(&sy.prod[j], cons + 1, &sy.abort)) {
+          ok = false;
+          break;
+        }
+        const float score = ring[j][cons % WS_RING][l];
+        mem_order();
+        ++cons;
+        lds_store(&sy.cons[j], cons);
+        const int jj = t * PF_KTILE + l;
+        wave_offer<MODE>(st, score, (uint32_t)(part + a.P * jj), jj < vis, a, hist, list);
+      }
+      if (!ok) break;
+      finish_row<MODE>(a, st, b, row, part, hist, list);
+    }
   }
 }
 
@@ -368,7 +683,7 @@ __device__ __forceinline__ float ld_f32<__bf16>(const __bf16* p, size_t i) { ret
 
 template <int MODE, typename Tin>
 __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs a) {
-  __shared__ uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
   __shared__ u64 list_all[PF_THREADS / WAVE][WAVE_LIST];
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   uint32_t* hist = hist_all[wv];
@@ -511,7 +826,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs
 constexpr int DEC_REG = 32;                              // keys per lane: rows up to 32768 in registers
 
 __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeArgs a) {
-  __shared__ uint32_t hist[SEL_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[SEL_BINS];
   __shared__ u64 red[2 * DEC_SEL_THREADS / WAVE];
   __shared__ u64 list[BLOCK_LIST];
   __shared__ int wcnt[DEC_SEL_THREADS / WAVE];
@@ -695,23 +1010,24 @@ __global__ __launch_bounds__(RECALL_THREADS) void recall_kernel(const int32_t* s
 // ============================================================ launchers
 
 template <int MODE>
-static const void* prefill_kernel_ptr(bool mfma, bool bf16) {
-  if (mfma) return (const void*)prefill_mfma_kernel<MODE>;
+static const void* prefill_kernel_ptr(bool mfma, bool bf16, bool ws) {
+  if (mfma) return ws ? (const void*)prefill_ws_kernel<MODE> : (const void*)prefill_mfma_kernel<MODE>;
   if (bf16) return (const void*)prefill_generic_kernel<MODE, __bf16>;
   return (const void*)prefill_generic_kernel<MODE, float>;
 }
 
-static const void* prefill_kernel_for(int mode, bool mfma, bool bf16) {
+static const void* prefill_kernel_for(int mode, bool mfma, bool bf16, bool ws) {
   switch (mode) {
-    case MODE_TOPK: return prefill_kernel_ptr<MODE_TOPK>(mfma, bf16);
-    case MODE_THRESHOLD: return prefill_kernel_ptr<MODE_THRESHOLD>(mfma, bf16);
-    default: return prefill_kernel_ptr<MODE_INTERLEAVED>(mfma, bf16);
+    case MODE_TOPK: return prefill_kernel_ptr<MODE_TOPK>(mfma, bf16, ws);
+    case MODE_THRESHOLD: return prefill_kernel_ptr<MODE_THRESHOLD>(mfma, bf16, ws);
+    default: return prefill_kernel_ptr<MODE_INTERLEAVED>(mfma, bf16, ws);
   }
 }
 
-int prefill_blocks_per_cu(int mode, bool mfma, bool bf16) {
+int prefill_blocks_per_cu(int mode, bool mfma, bool bf16, bool ws) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel_for(mode, mfma, bf16), PF_THREADS, 0) !=
+  const int threads = mfma && ws ? WS_THREADS : PF_THREADS;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel_for(mode, mfma, bf16, ws), threads, 0) !=
           hipSuccess ||
       n < 1)
     n = 1;
@@ -720,8 +1036,10 @@ int prefill_blocks_per_cu(int mode, bool mfma, bool bf16) {
 
 template <int MODE>
 static void launch_prefill_mode(const PrefillArgs& a, bool mfma, int grid, hipStream_t st) {
-  if (mfma)
+  if (mfma && !a.wave_spec)
     prefill_mfma_kernel<MODE><<<grid, PF_THREADS, 0, st>>>(a);
+  else if (mfma)
+    prefill_ws_kernel<MODE><<<grid, WS_THREADS, 0, st>>>(a);
   else if (a.bf16)
     prefill_generic_kernel<MODE, __bf16><<<grid, PF_THREADS, 0, st>>>(a);
   else
