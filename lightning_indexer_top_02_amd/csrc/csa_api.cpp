@@ -97,6 +97,8 @@ struct PrefillPlan {
   size_t cand_bytes, sort_bytes, total;
 };
 
+// Workspace layout: [ws_slots workgroups x PF_ROWS candidate buffers of C
+// keys][sort scratch when CSA_SORTED].
 PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, uint32_t flags) {
   PrefillPlan pl;
   pl.nqb = (p->S_q + csa::PF_ROWS - 1) / csa::PF_ROWS;
@@ -134,14 +136,14 @@ int device_cus() {
   return n;
 }
 
-int occupancy_cached(int mode, bool mfma, bool bf16, bool ws) {
+int occupancy_cached(int mode, bool mfma, bool bf16) {
   static std::mutex mu;
-  static int cache[64][3][2][2][2];
+  static int cache[64][3][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   std::lock_guard<std::mutex> g(mu);
-  int& c = cache[dev][mode][mfma][bf16][ws];
-  if (c == 0) c = csa::prefill_blocks_per_cu(mode, mfma, bf16, ws);
+  int& c = cache[dev][mode][mfma][bf16];
+  if (c == 0) c = csa::prefill_blocks_per_cu(mode, mfma, bf16);
   return c;
 }
 
@@ -170,10 +172,8 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
   a.C = pl.C;
   a.need_scores = score_dst != nullptr;
   a.bf16 = p->dtype == CSA_BF16;
-  // CSA_PREFILL_KERNEL=ws selects the wave-specialised MFMA kernel (same results)
-  a.wave_spec = env_is("CSA_PREFILL_KERNEL", "ws") ? 1 : 0;
 
-  const int resident = device_cus() * occupancy_cached(mode, mfma, a.bf16, a.wave_spec != 0);
+  const int resident = device_cus() * occupancy_cached(mode, mfma, a.bf16);
   const int grid = std::max(1, std::min(pl.ws_slots, resident));
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = csa::launch_prefill(a, mode, mfma, grid, st);

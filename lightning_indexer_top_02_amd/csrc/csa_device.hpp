@@ -217,15 +217,18 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 }
 
 // Linear score bins between the smallest and largest score of a key set.
-// Monotone in the score (IEEE subtraction, multiplication, fminf and the
-// truncating conversion never reverse an order), so every key in a higher
+// Monotone in the score (IEEE subtraction, multiplication, the truncating
+// conversion and the integer clamp never reverse an order), so every key in a higher
 // bin beats every key in a lower one: the bin holding rank k is the only one
 // that needs exact resolution.  Scores of typical rows share a few exponents,
 // which would crowd a first radix digit on raw bits into a handful of bins.
 struct LinBins {
   float lo, scale;
+  // (key_score(key) - lo) * scale >= 0 for every key of the set: truncate,
+  // then clamp the top bin as an integer (no float min and its canonicalize)
   __device__ __forceinline__ int operator()(u64 key) const {
-    return (int)fminf((key_score(key) - lo) * scale, (float)(SEL_BINS - 1));
+    const uint32_t b = (uint32_t)((key_score(key) - lo) * scale);
+    return (int)(b < (uint32_t)(SEL_BINS - 1) ? b : (uint32_t)(SEL_BINS - 1));
   }
 };
 
@@ -248,18 +251,34 @@ struct InBin {
   __device__ __forceinline__ bool operator()(u64 v) const { return v != 0ull && lb(v) == bin; }
 };
 
-// Exact k-th largest of the keys in x accepted by `in` (more than k of them)
-// by most-significant-digit radix refinement from registers.
-template <int R, typename Pred>
-__device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, Pred in) {
-  const int l = lane_id();
+// Exact k-th largest of the keys accepted by `in` (more than k of them) by
+// most-significant-digit radix refinement from registers.  key(j) returns
+// the key of element j*WAVE + lane (0 = empty), for j < R with j*WAVE < n; it
+// is recomputed on every pass, so a caller may keep its keys in any compact
+// form.
+// A uniform bound re-read at the start of a pass: the compiler then compares
+// slot indices against it afresh in each pass instead of keeping one
+// 64-bit condition per slot alive across passes (which spills).
+// (n is the same in every lane.)
+__device__ __forceinline__ int fresh_bound(int n) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  asm volatile("" : "+s"(n));
+  return n;
+}
+
+template <int R, typename KeyAt, typename Pred>
+__device__ __forceinline__ u64 wave_radix_kth_at(KeyAt key, int n, int k, uint32_t* hist, Pred in) {
   u64 lo = ~0ull, hi = 0ull;
+  key.fresh();
+  int nn = fresh_bound(n);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const u64 v = x[j];
-    if (j * WAVE < n && in(v)) {
-      lo = v < lo ? v : lo;
-      hi = v > hi ? v : hi;
+    if (j * WAVE < nn) {
+      const u64 v = key(j);
+      if (in(v)) {
+        lo = v < lo ? v : lo;
+        hi = v > hi ? v : hi;
+      }
     }
   }
   lo = wave_min_u64(lo);
@@ -275,10 +294,12 @@ __device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, u
     const uint32_t dmask = (uint32_t)(nb - 1);
     wave_clear_hist(hist, nb);
     wave_lds_sync();
+    key.fresh();
+    nn = fresh_bound(n);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      if (j * WAVE < n) {
-        const u64 v = x[j];
+      if (j * WAVE < nn) {
+        const u64 v = key(j);
         const bool match = in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix);
         if (match) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
       }
@@ -291,6 +312,23 @@ __device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, u
     hi_bit = shift;
     if (pk.count == rank || shift == 0) return prefix << shift;
   }
+}
+
+// Key accessors for the register selects.  fresh() runs at the start of
+// every pass over the keys: an accessor that derives keys from a compact form
+// launders its base there, so that the compiler recomputes the per-slot
+// values in each pass instead of keeping all of them live across passes.
+template <int R>
+struct ArrayKeys {
+  const u64 (&x)[R];
+  __device__ __forceinline__ u64 operator()(int j) const { return x[j]; }
+  __device__ __forceinline__ void fresh() {}
+};
+
+// The same over keys held as an array.
+template <int R, typename Pred>
+__device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, Pred in) {
+  return wave_radix_kth_at<R>(ArrayKeys<R>{x}, n, k, hist, in);
 }
 
 // Exact k-th largest of the n keys held in x (n > k >= 1): linear-bin
@@ -343,6 +381,21 @@ __device__ __forceinline__ u64 wave_select_kth_regs(const u64 (&x)[R], int n, in
   return wave_radix_kth(y, w, r, hist, AnyKey{});
 }
 
+// The r-th largest of w distinct keys list[0..w) (1 <= r <= w <= WAVE_LIST).
+__device__ __forceinline__ u64 wave_list_kth(const u64* list, int w, int r, uint32_t* hist) {
+  const int l = lane_id();
+  if (w <= WAVE) return wave_small_kth(list, w, r);
+  constexpr int RL = WAVE_LIST / WAVE;
+  u64 y[RL];
+#pragma unroll
+  for (int j = 0; j < RL; ++j) {
+    const int i = j * WAVE + l;
+    y[j] = i < w ? list[i] : 0ull;
+  }
+  wave_lds_sync();
+  return wave_radix_kth(y, w, r, hist, AnyKey{});
+}
+
 // ---------------------------------------------------------------- streaming select
 //
 // The same selection over keys in global memory written earlier by this
@@ -355,12 +408,18 @@ template <typename F>
 __device__ __forceinline__ void wave_stream(const u64* buf, int n, F f) {
   const int l = lane_id();
   for (int base = 0; base < n; base += STREAM_BATCH * WAVE) {
+    // Unconditional loads from clamped addresses, so that the whole batch is in
+    // flight at once (a load under an i < n branch is waited on by itself);
+    // candidate buffers stream past L2.
     u64 v[STREAM_BATCH];
 #pragma unroll
     for (int j = 0; j < STREAM_BATCH; ++j) {
       const int i = base + j * WAVE + l;
-      v[j] = i < n ? __builtin_nontemporal_load(&buf[i]) : 0ull;   // candidate buffers stream past L2
+      v[j] = __builtin_nontemporal_load(&buf[i < n ? i : n - 1]);
     }
+#pragma unroll
+    for (int j = 0; j < STREAM_BATCH; ++j)
+      if (base + j * WAVE + l >= n) v[j] = 0ull;
 #pragma unroll
     for (int j = 0; j < STREAM_BATCH; ++j) f(v[j], base + j * WAVE);   // 0 = past the end
   }

@@ -35,11 +35,10 @@ struct PrefillArgs {
   float* out_score;     // may be null
   int32_t* out_count;   // threshold mode
   int out_stride;       // entries per output row (kk, or P*kk when interleaved)
-  unsigned long long* cand;      // [grid][PF_ROWS][C]
+  unsigned long long* cand;      // [grid][PF_ROWS][C] candidate buffers, one per wave
   int C;                // candidate capacity per query row, >= kk + 64
   int need_scores;      // out_score != null
   int bf16;             // element type of q and k: 1 = bf16, 0 = fp32
-  int wave_spec;        // MFMA path: 1 = wave-specialised kernel, 0 = single-role kernel
 };
 
 struct DecodeArgs {
@@ -64,7 +63,7 @@ constexpr int DEC_SEL_THREADS = 1024;
 // mfma: the bf16 H=64 D=128 MFMA kernel; otherwise the generic kernel for a.bf16.
 hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, hipStream_t st);
 // Resident workgroups per CU of the chosen prefill kernel (>= 1).
-int prefill_blocks_per_cu(int mode, bool mfma, bool bf16, bool ws);
+int prefill_blocks_per_cu(int mode, bool mfma, bool bf16);
 hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st);
 hipError_t launch_sort_rows(int32_t* idx, float* score, long long rows, int len, hipStream_t st);
 hipError_t launch_recall(const int32_t* sel, int n_sel, const int32_t* ref, int n_ref,

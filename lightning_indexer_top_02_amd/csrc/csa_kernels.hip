@@ -60,9 +60,10 @@ struct Slot {
 };
 
 // Candidate buffers and output rows are written once and read at most once
-// more by the same wave: their loads and stores are non-temporal, so that
-// they stream past L2 instead of evicting the key tiles every workgroup
-// re-reads there.
+// more: their loads and stores are non-temporal, so that they stream past L2
+// instead of evicting the key tiles every workgroup re-reads there.  (Dense
+// score rows, read back right after by the select kernel, stay cacheable:
+// measured faster.)
 
 // Inclusive key bound X (keys >= X pass) as a (score, index) threshold.
 __device__ __forceinline__ void key_to_thr(u64 X, float& ts, uint32_t& ti) {
@@ -129,44 +130,142 @@ __device__ __forceinline__ void emit_key(u64 x, int pos, int kk, int32_t* oi, fl
   }
 }
 
-// Candidate buffers up to this size are selected from registers at the end
-// of a row: one load pass with every load in flight instead of three
-// latency-bound streaming passes (the MFMA operands are dead by then).
+// Candidate buffers up to this size are selected from registers: one load
+// pass with every load in flight instead of three latency-bound streaming
+// passes.
 constexpr int EMIT_REGS = 66;
 
-// Emit the exact top-kk of buf[0..cnt) (all of it when cnt <= kk) to one
-// output row of kk entries, then pad with -1 / -inf.
-__device__ __forceinline__ void wave_emit(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi, float* os) {
+// Emit the exact top-kk of the n_keys nonzero keys key(j) (all of them when
+// n_keys <= kk; key(j) is the key of element j*WAVE + lane for j*WAVE < n, 0
+// = empty) to one output row, in no particular order; returns the number
+// written.  lo/hi: per-lane score bounds of the nonzero keys.  One histogram
+// pass over linear score bins finds the bin holding rank kk; one more pass
+// emits every key of a higher bin and gathers the bin's own keys into `list`,
+// whose top r are resolved exactly and emitted last.  Keys are recomputed by
+// key(j) on each pass, so callers may hold them in a compact form.
+template <int R, typename KeyAt>
+__device__ __forceinline__ int wave_emit_keys_at(KeyAt key, int n, int n_keys, int kk, uint32_t* hist, u64* list,
+                                                 float lo, float hi, int32_t* oi, float* os) {
   const int l = lane_id();
   int w = 0;
+  auto emit_ge = [&](u64 T) {                          // every key >= T (T >= 1 skips empty slots)
+    key.fresh();
+    const int nn = fresh_bound(n);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j * WAVE < nn) {
+        const u64 v = key(j);
+        const bool keep = v >= T;
+        const u64 m = ballot(keep);
+        if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
+        w += __popcll(m);
+      }
+      __builtin_amdgcn_sched_barrier(0);               // one slot at a time: short mask live ranges
+    }
+    return w < kk ? w : kk;
+  };
+  if (n_keys <= kk) return emit_ge(1ull);
+  lo = wave_min_f32(lo);
+  hi = wave_max_f32(hi);
+  LinBins lb;
+  if (!lin_bins_ok(lo, hi, lb)) return emit_ge(wave_radix_kth_at<R>(key, n, kk, hist, AnyKey{}));
+  wave_clear_hist(hist, SEL_BINS);
+  wave_lds_sync();
+  key.fresh();
+  int nn = fresh_bound(n);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * WAVE < nn) {
+      const u64 v = key(j);
+      if (v) atomicAdd(&hist[lb(v)], 1u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wave_lds_sync();
+  const BinPick pk = wave_pick_bin(hist, SEL_BINS, kk);
+  wave_lds_sync();
+  const int r = kk - pk.above;
+  if (pk.count > WAVE_LIST || pk.count < r)           // crowded bin (or inconsistent counts): exact radix
+    return emit_ge(wave_radix_kth_at<R>(key, n, r, hist, InBin{lb, pk.bin}));
+  int lc = 0;
+  key.fresh();
+  nn = fresh_bound(n);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * WAVE < nn) {
+      const u64 v = key(j);
+      const int bin = v ? lb(v) : -1;
+      const bool up = bin > pk.bin, at = bin == pk.bin;
+      const u64 mu = ballot(up), ma = ballot(at);
+      if (up) emit_key(v, w + lanes_below(mu), kk, oi, os);
+      if (at) list[lc + lanes_below(ma)] = v;
+      w += __popcll(mu);
+      lc += __popcll(ma);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wave_lds_sync();
+  // the boundary bin: its top r keys (lc >= r keys, all distinct)
+  const u64 T = r == lc ? 1ull : wave_list_kth(list, lc, r, hist);
+  for (int base = 0; base < lc; base += WAVE) {
+    const int i = base + l;
+    const u64 v = i < lc ? list[i] : 0ull;
+    const bool keep = i < lc && v >= T;
+    const u64 m = ballot(keep);
+    if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
+    w += __popcll(m);
+  }
+  wave_lds_sync();
+  return w < kk ? w : kk;
+}
+
+template <int R>
+__device__ __forceinline__ int wave_emit_keys_regs(const u64 (&x)[R], int n, int n_keys, int kk, uint32_t* hist,
+                                                   u64* list, float lo, float hi, int32_t* oi, float* os) {
+  return wave_emit_keys_at<R>(ArrayKeys<R>{x}, n, n_keys, kk, hist, list, lo, hi, oi, os);
+}
+
+__device__ __forceinline__ int wave_emit_cand_stream(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi,
+                                                     float* os);
+
+// Emit the exact top-kk of the candidate list buf[0..cnt) (all of it when
+// cnt <= kk); returns the number written.
+__device__ __forceinline__ int wave_emit_cand(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi,
+                                              float* os) {
+  const int l = lane_id();
+  wave_own_stores_visible();
   if (st.cnt <= EMIT_REGS * WAVE) {
-    wave_own_stores_visible();
     u64 x[EMIT_REGS];
 #pragma unroll
     for (int j = 0; j < EMIT_REGS; ++j) {
       const int i = j * WAVE + l;
-      x[j] = i < st.cnt ? __builtin_nontemporal_load(&st.cand[i]) : 0ull;
+      x[j] = __builtin_nontemporal_load(&st.cand[i < st.cnt ? i : (st.cnt > 0 ? st.cnt - 1 : 0)]);
     }
-    const u64 T = st.cnt > kk ? wave_select_kth_regs(x, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
 #pragma unroll
-    for (int j = 0; j < EMIT_REGS; ++j) {
-      const bool keep = x[j] >= T;                     // T >= 1 excludes empty slots
-      const u64 m = ballot(keep);
-      if (keep) emit_key(x[j], w + lanes_below(m), kk, oi, os);
-      w += __popcll(m);
-    }
-  } else {
-    const u64 T = st.cnt > kk ? wave_select_kth_stream(st.cand, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
-    wave_own_stores_visible();
-    wave_stream(st.cand, st.cnt, [&](u64 v, int) {
-      const bool keep = v >= T;                        // T >= 1 excludes slots past the end
-      const u64 m = ballot(keep);
-      if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
-      w += __popcll(m);
-    });
+    for (int j = 0; j < EMIT_REGS; ++j)                 // (unconditional loads above: all in flight)
+      if (j * WAVE + l >= st.cnt) x[j] = 0ull;
+    return wave_emit_keys_regs(x, st.cnt, st.cnt, kk, hist, list, st.lo, st.hi, oi, os);
   }
-  w = w < kk ? w : kk;
-  for (int i = w + l; i < kk; i += WAVE) {
+  return wave_emit_cand_stream(st, kk, hist, list, oi, os);
+}
+
+// The same by streaming the buffer (any length; registers stay free).
+__device__ __forceinline__ int wave_emit_cand_stream(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi,
+                                                     float* os) {
+  const u64 T = st.cnt > kk ? wave_select_kth_stream(st.cand, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
+  int w = 0;
+  wave_stream(st.cand, st.cnt, [&](u64 v, int) {
+    const bool keep = v >= T;                          // T >= 1 excludes slots past the end
+    const u64 m = ballot(keep);
+    if (keep) emit_key(v, w + lanes_below(m), kk, oi, os);
+    w += __popcll(m);
+  });
+  return w < kk ? w : kk;
+}
+
+// Pad an output row after its first w entries with -1 / -inf.
+__device__ __forceinline__ void wave_pad_row(int w, int kk, int32_t* oi, float* os) {
+  for (int i = w + lane_id(); i < kk; i += WAVE) {
     oi[i] = -1;
     if (os) os[i] = -__builtin_inff();
   }
@@ -215,12 +314,13 @@ __device__ __forceinline__ void finish_row(const PrefillArgs& a, Slot& st, int b
   if (row >= a.S_q) return;
   const size_t orow = (size_t)b * a.S_q + row;
   float* os = a.out_score ? a.out_score + orow * a.out_stride + (size_t)part * a.kk : nullptr;
-  wave_emit(st, a.kk, hist, list, out_row(a, b, row, part), os);
+  int32_t* oi = out_row(a, b, row, part);
+  wave_pad_row(wave_emit_cand(st, a.kk, hist, list, oi, os), a.kk, oi, os);
   if (MODE == MODE_THRESHOLD && lane_id() == 0) a.out_count[orow] = st.surv;
 }
 
-__device__ __forceinline__ void slot_init(Slot& st, const PrefillArgs& a, int wv, int mode) {
-  st.cand = a.cand + ((size_t)blockIdx.x * PF_ROWS + wv) * a.C;
+__device__ __forceinline__ void slot_init(Slot& st, u64* cand, const PrefillArgs& a, int mode) {
+  st.cand = cand;
   st.cnt = 0;
   key_to_thr(mode == MODE_THRESHOLD ? a.thr_fixed : 0ull, st.thr_s, st.thr_i);
   st.surv = 0;
@@ -229,36 +329,6 @@ __device__ __forceinline__ void slot_init(Slot& st, const PrefillArgs& a, int wv
 }
 
 // ============================================================ LDS staging helpers
-
-constexpr int WS_SPIN_LIMIT = 1 << 22;          // bounded spins: about 0.3 s before giving up
-
-__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }   // compiler-only barrier
-// Empty register constraint: the value must exist in a VGPR at this point of the schedule.
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-
-__device__ __forceinline__ int lds_load(int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
-// One add per wave (lane 0): executed by every lane it would count 64 times.
-__device__ __forceinline__ void lds_add(int* p, int v) {
-  if (lane_id() == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_store(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Wait until *ctr >= target; false if the workgroup aborted (or this wait ran out).
-__device__ __forceinline__ bool spin_ge(int* ctr, int target, int* abort) {
-  int n = 0;
-  while (lds_load(ctr) < target) {
-    if (lds_load(abort)) return false;
-    if (++n > WS_SPIN_LIMIT) {
-      lds_store(abort, 1);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  mem_order();
-  return true;
-}
 
 // s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding)
 template <int N>
@@ -272,13 +342,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 l
-// (lds is the same in every lane).
-// Written as asm so that the compiler does not treat every later LDS access
-// as a possible reader of the in-flight load (it would drain vmcnt to 0 before
-// each one); the caller orders the data with explicit vmcnt waits instead.
-// The instruction has no register results (only its address operand, read at
-// issue), and this kernel holds nothing else in M0 (only these sequences
-// write it), so clobbering M0 here is safe.
+// (lds is the same in every lane).  Written as asm so that the compiler does
+// not treat every later LDS access as a possible reader of the in-flight load
+// (it would drain vmcnt to 0 before each one); the caller orders the data
+// with explicit vmcnt waits instead.  The instruction has no register results
+// (only its address operand, read at issue), and the kernel using it holds
+// nothing else in M0 (only these sequences write it), so clobbering M0 here
+// is safe.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform LDS base
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
@@ -294,7 +364,9 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 // the head weights are applied in registers; exchanging the two column tiles'
 // half-wave partial sums leaves lanes 0-31 with the scores of tile 0 and lanes
 // 32-63 with those of tile 1.  Two workgroups share a CU (two waves per SIMD),
-// so one wave's VALU epilogue overlaps the other's MFMAs.
+// so one wave's VALU epilogue overlaps the other's MFMAs.  Each wave filters
+// its row's scores into a candidate list (compacted to the top-kk when full)
+// and selects the row's final top-kk from it at the end of the query block.
 
 constexpr int MH = 64, MD = 128;
 // A key tile (PF_KTILE keys x 256 B) sits in LDS as groups of 16 keys; inside
@@ -356,7 +428,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
       for (int i = 0; i < 16; ++i) wl[rt][i] = wrow[8 * (i >> 2) + (i & 3)];
     }
     Slot st;
-    slot_init(st, a, wv, MODE);
+    slot_init(st, a.cand + ((size_t)blockIdx.x * PF_ROWS + wv) * a.C, a, MODE);
 
     const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
     const size_t kseq = (size_t)b * a.T;
@@ -368,8 +440,7 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
       if ((long long)part + (long long)a.P * (t * PF_KTILE + PF_KTILE - 1) < a.T) {
         const char* base = (const char*)(K + row0 * MD);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dma16(base + doff[e], lds_addr(&ktile[buf][(e * 4 + wv) * 1024]));
+        for (int e = 0; e < 4; ++e) dma16(base + doff[e], lds_addr(&ktile[buf][(e * 4 + wv) * 1024]));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -390,10 +461,19 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
     __syncthreads();
 
     // Step t covers keys [64t, 64t+64): column tile 0 = keys 64t + (l & 31),
-    // column tile 1 = keys 64t + 32 + (l & 31).
+    // column tile 1 = keys 64t + 32 + (l & 31).  The scores of tile t are
+    // offered during step t+1, after its key-tile load is issued: the offer's
+    // global stores then have a whole step to complete before the vmcnt wait
+    // at its end.
+    float pend = 0.f;
+    auto flush = [&](int t) {
+      const int j = t * PF_KTILE + l;
+      wave_offer<MODE>(st, pend, (uint32_t)(part + a.P * j), j < vis, a, hist, list);
+    };
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
       if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+      if (t > 0) flush(t - 1);
       const char* kb = &ktile[buf][b_off];
       f32x16 acc[2][2];
 #pragma unroll
@@ -430,241 +510,12 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
           for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[c][rt][i]), ps);
         part2[c] = ps;
       }
-      const float score = half_swap_sum(part2[0], part2[1]);
-      const int j = t * PF_KTILE + l;
-      wave_offer<MODE>(st, score, (uint32_t)(part + a.P * j), j < vis, a, hist, list);
+      pend = half_swap_sum(part2[0], part2[1]);
       wait_vmcnt<0>();                                 // this wave's part of tile t+1 landed
       __syncthreads();                                 // all of tile t+1 landed and stage t is free
     }
+    if (ntiles > 0) flush(ntiles - 1);
     finish_row<MODE>(a, st, b, row, part, hist, list);
-  }
-}
-
-// ============================================================ wave-specialised MFMA prefill
-//
-// Same scores and selection as prefill_mfma_kernel, with the work split by
-// role inside a workgroup of 8 waves (one workgroup per CU):
-//   waves 0-3  "score waves": MFMA + ReLU/weights for query row j = wave; they
-//              push each 64-key tile of scores into an LDS ring and never
-//              touch global memory after loading their query;
-//   waves 4-7  "select waves": for row j = wave-4 they pop score tiles, filter
-//              and append candidates, compact, and run the final select while
-//              the score waves already work on the next query block.
-// No s_barrier inside the loop.  Key tiles rotate through WS_NS LDS stages;
-// the score waves coordinate them with per-stage LDS counters (loads landed,
-// reads done), and each score/select pair shares the ring's produced and
-// consumed counters.  Every wait is a bounded spin; a spin that runs out sets
-// an abort flag that ends all waves of the workgroup.
-
-constexpr int WS_THREADS = 512;
-constexpr int WS_NS = 4;                      // key-tile stages (tiles t+1..t+3 in flight at step t)
-constexpr int WS_RING = 32;                   // score tiles buffered per row
-
-struct WsSync {
-  int kfill[WS_NS];  // per stage: completed (wave, tile) loads
-  int kfree[WS_NS];  // per stage: completed (wave, tile) reads
-  int prod[PF_ROWS]; // per row: score tiles pushed
-  int cons[PF_ROWS]; // per row: score tiles popped
-  int abort;
-};
-
-template <int MODE>
-__global__ __launch_bounds__(WS_THREADS, 1) void prefill_ws_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kst[WS_NS][KT_BYTES];
-  __shared__ float ring[PF_ROWS][WS_RING][WAVE];
-  __shared__ __attribute__((aligned(16))) uint32_t hist_all[PF_ROWS][SEL_BINS];
-  __shared__ u64 list_all[PF_ROWS][WAVE_LIST];
-  __shared__ WsSync sy;
-
-  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
-  if (tid < (int)(sizeof(WsSync) / sizeof(int))) ((int*)&sy)[tid] = 0;
-  __syncthreads();
-
-  if (wv < PF_ROWS) {
-    // ------------------------------------------------------------ score wave
-    const int j = wv;
-    const __bf16* Q = (const __bf16*)a.q;
-    const __bf16* K = (const __bf16*)a.k;
-    const int b_off = ((l >> 4) & 1) * 4096 + (l >> 5) * 256 + (l & 15) * 16;
-    const uint32_t kst_lds = lds_addr(&kst[0][0]);
-    uint32_t doff[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int blk = e * 4 + j, row = (blk >> 2) * 16 + (l & 15), chunk = (blk & 3) * 4 + (l >> 4);
-      doff[e] = (uint32_t)(((size_t)row * a.P * MD + chunk * 8) * 2);
-    }
-    int gt = 0;                                       // key tiles loaded so far (same in all score waves)
-    int prod = 0;                                     // score tiles pushed for row j
-    for (int r = 0;; ++r) {
-      const int it = round_item(r);
-      if (r * (int)gridDim.x >= a.n_items) break;
-      if (it >= a.n_items) continue;
-      int b, qb, part;
-      decode_item(a, it, b, qb, part);
-      int vis_max;
-      if (!block_needs_scores<MODE>(a, b, qb, part, vis_max)) continue;
-      const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
-      if (ntiles == 0) continue;
-      const int row = qb * PF_ROWS + j;
-      const int rq = row < a.S_q ? row : a.S_q - 1;
-      bf16x8 A[2][8];
-      float wl[2][16];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8* src = (const bf16x8*)(Q + (((size_t)b * a.S_q + rq) * MH + rt * 32 + (l & 31)) * MD);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
-        const float* wrow = a.w + ((size_t)b * a.S_q + rq) * MH + rt * 32 + 4 * (l >> 5);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) wl[rt][i] = wrow[8 * (i >> 2) + (i & 3)];
-      }
-      // Drain the query loads here: the compiler knows nothing of the key-tile
-      // loads below, and a query load it still counted as pending would make it
-      // wait inside the tile loop for every load in flight.
-      wait_vmcnt<0>();
-      const size_t kseq = (size_t)b * a.T;
-      const int n0 = gt;                              // tile t of this item is global tile n0 + t
-      // tile t -> stage (n0 + t) % WS_NS, its use number in that stage (n0 + t) / WS_NS
-      auto fill = [&](int t) -> bool {                // wait for the stage to be free, then load tile t
-        const int n = n0 + t, s = n % WS_NS;
-        if (!spin_ge(&sy.kfree[s], PF_ROWS * (n / WS_NS), &sy.abort)) return false;
-        const uint32_t lds = kst_lds + s * KT_BYTES + j * 1024;
-        const size_t row0 = kseq + (size_t)part + (size_t)a.P * (size_t)(t * PF_KTILE);
-        if ((long long)part + (long long)a.P * (t * PF_KTILE + PF_KTILE - 1) < a.T) {
-          const char* base = (const char*)(K + row0 * MD);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dma16(base + doff[e], lds + e * 4096);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int blk = e * 4 + j, grp = blk >> 2, quad = blk & 3;
-            int jj = t * PF_KTILE + grp * 16 + (l & 15);
-            jj = jj < vis_max ? jj : vis_max - 1;
-            const int chunk = quad * 4 + (l >> 4);
-            dma16(K + (kseq + (size_t)part + (size_t)a.P * jj) * MD + chunk * 8, lds + e * 4096);
-          }
-        }
-        return true;
-      };
-      // tile t has landed for this wave once at most `later` newer tiles are in flight
-      auto publish = [&](int t, int later) -> bool {
-        if (later >= 2) wait_vmcnt<8>();
-        else if (later == 1) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-        mem_order();
-        const int n = n0 + t, s = n % WS_NS;
-        lds_add(&sy.kfill[s], 1);
-        return spin_ge(&sy.kfill[s], PF_ROWS * (n / WS_NS + 1), &sy.abort);
-      };
-      auto stage = [&](int t) { return (const char*)&kst[(n0 + t) % WS_NS][0] + b_off; };
-      f32x16 acc0[2], acc1[2];
-      auto mma = [&](const char* kb, f32x16 (&acc)[2]) {
-        acc[0] = f32x16{};
-        acc[1] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 bb = *(const bf16x8*)(kb + kk * 512);
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0][kk], bb, acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1][kk], bb, acc[1], 0, 0, 0);
-        }
-      };
-      auto epi = [&](const f32x16 (&acc)[2]) {
-        float ps = 0.f;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[rt][i]), ps);
-        return ps;
-      };
-      // epilogue of the previous half tile interleaved with the MFMAs of the next
-      auto phase = [&](const char* kb, f32x16 (&acc_new)[2], const f32x16 (&acc_old)[2]) {
-        float ps = epi(acc_old);
-        mma(kb, acc_new);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        pin(ps);
-        return ps;
-      };
-      bool ok = true;
-      const int pre = ntiles < WS_NS - 1 ? ntiles : WS_NS - 1;
-      for (int t = 0; ok && t < pre; ++t) ok = fill(t);
-      if (ok) ok = publish(0, pre - 1);
-      if (ok) mma(stage(0), acc0);
-      for (int t = 0; ok && t < ntiles; ++t) {
-        const float p0 = phase(stage(t) + 8192, acc1, acc0);   // second half of tile t
-        __builtin_amdgcn_sched_barrier(0);
-        mem_order();
-        lds_add(&sy.kfree[(n0 + t) % WS_NS], 1);              // done reading tile t
-        float p1;
-        if (t + 1 < ntiles) {
-          if (t + WS_NS - 1 < ntiles && !(ok = fill(t + WS_NS - 1))) break;
-          const int last = t + WS_NS - 1 < ntiles - 1 ? t + WS_NS - 1 : ntiles - 1;
-          if (!(ok = publish(t + 1, last - (t + 1)))) break;
-          __builtin_amdgcn_sched_barrier(0);
-          p1 = phase(stage(t + 1), acc0, acc1);                 // first half of tile t+1
-        } else {
-          p1 = epi(acc1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const float score = half_swap_sum(p0, p1);
-        // push the tile of 64 scores to the select wave of row j
-        if (!(ok = spin_ge(&sy.cons[j], prod + 1 - WS_RING, &sy.abort))) break;
-        ring[j][prod % WS_RING][l] = score;
-        mem_order();
-        ++prod;
-        lds_store(&sy.prod[j], prod);
-      }
-      gt += ntiles;
-      if (!ok) {
-        wait_vmcnt<0>();                              // no load left in flight at exit
-        break;
-      }
-    }
-  } else {
-    // ------------------------------------------------------------ select wave
-    const int j = wv - PF_ROWS;
-    uint32_t* hist = hist_all[j];
-    u64* list = list_all[j];
-    int cons = 0;
-    for (int r = 0;; ++r) {
-      const int it = round_item(r);
-      if (r * (int)gridDim.x >= a.n_items) break;
-      if (it >= a.n_items) continue;
-      int b, qb, part;
-      decode_item(a, it, b, qb, part);
-      int vis_max;
-      const bool need = block_needs_scores<MODE>(a, b, qb, part, vis_max);
-      const int row = qb * PF_ROWS + j;
-      const int vis = row_visible(a, b, row, part);
-      if (!need) {
-        if (row < a.S_q) wave_emit_all_visible(a, b, row, part, vis);
-        continue;
-      }
-      const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
-      Slot st;
-      slot_init(st, a, j, MODE);
-      bool ok = true;
-      for (int t = 0; t < ntiles; ++t) {
-        if (!spin_ge(&sy.prod[j], cons + 1, &sy.abort)) {
-          ok = false;
-          break;
-        }
-        const float score = ring[j][cons % WS_RING][l];
-        mem_order();
-        ++cons;
-        lds_store(&sy.cons[j], cons);
-        const int jj = t * PF_KTILE + l;
-        wave_offer<MODE>(st, score, (uint32_t)(part + a.P * jj), jj < vis, a, hist, list);
-      }
-      if (!ok) break;
-      finish_row<MODE>(a, st, b, row, part, hist, list);
-    }
   }
 }
 
@@ -707,7 +558,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs
       continue;
     }
     Slot st;
-    slot_init(st, a, wv, MODE);
+    slot_init(st, a.cand + ((size_t)blockIdx.x * PF_ROWS + wv) * a.C, a, MODE);
     const size_t qoff = ((size_t)b * a.S_q + row) * a.H;
     for (int j0 = 0; j0 < vis; j0 += WAVE) {
       const int j = j0 + l;
@@ -1010,36 +861,32 @@ __global__ __launch_bounds__(RECALL_THREADS) void recall_kernel(const int32_t* s
 // ============================================================ launchers
 
 template <int MODE>
-static const void* prefill_kernel_ptr(bool mfma, bool bf16, bool ws) {
-  if (mfma) return ws ? (const void*)prefill_ws_kernel<MODE> : (const void*)prefill_mfma_kernel<MODE>;
+static const void* prefill_kernel_ptr(bool mfma, bool bf16) {
+  if (mfma) return (const void*)prefill_mfma_kernel<MODE>;
   if (bf16) return (const void*)prefill_generic_kernel<MODE, __bf16>;
   return (const void*)prefill_generic_kernel<MODE, float>;
 }
 
-static const void* prefill_kernel_for(int mode, bool mfma, bool bf16, bool ws) {
+static const void* prefill_kernel_for(int mode, bool mfma, bool bf16) {
   switch (mode) {
-    case MODE_TOPK: return prefill_kernel_ptr<MODE_TOPK>(mfma, bf16, ws);
-    case MODE_THRESHOLD: return prefill_kernel_ptr<MODE_THRESHOLD>(mfma, bf16, ws);
-    default: return prefill_kernel_ptr<MODE_INTERLEAVED>(mfma, bf16, ws);
+    case MODE_TOPK: return prefill_kernel_ptr<MODE_TOPK>(mfma, bf16);
+    case MODE_THRESHOLD: return prefill_kernel_ptr<MODE_THRESHOLD>(mfma, bf16);
+    default: return prefill_kernel_ptr<MODE_INTERLEAVED>(mfma, bf16);
   }
 }
 
-int prefill_blocks_per_cu(int mode, bool mfma, bool bf16, bool ws) {
+static int blocks_per_cu(const void* fn) {
   int n = 0;
-  const int threads = mfma && ws ? WS_THREADS : PF_THREADS;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel_for(mode, mfma, bf16, ws), threads, 0) !=
-          hipSuccess ||
-      n < 1)
-    n = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, PF_THREADS, 0) != hipSuccess || n < 1) n = 1;
   return n;
 }
 
+int prefill_blocks_per_cu(int mode, bool mfma, bool bf16) { return blocks_per_cu(prefill_kernel_for(mode, mfma, bf16)); }
+
 template <int MODE>
 static void launch_prefill_mode(const PrefillArgs& a, bool mfma, int grid, hipStream_t st) {
-  if (mfma && !a.wave_spec)
+  if (mfma)
     prefill_mfma_kernel<MODE><<<grid, PF_THREADS, 0, st>>>(a);
-  else if (mfma)
-    prefill_ws_kernel<MODE><<<grid, WS_THREADS, 0, st>>>(a);
   else if (a.bf16)
     prefill_generic_kernel<MODE, __bf16><<<grid, PF_THREADS, 0, st>>>(a);
   else

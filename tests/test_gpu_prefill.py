@@ -182,11 +182,14 @@ def test_config5_million_token_tail_sampled_rows():
     check_tolerance(p, rows, idx[:, rows], None, p["topk"])
 
 
-@pytest.mark.parametrize("case", ["compaction", "ragged", "kvlen_batch", "topk_gt_T", "many_items"])
-def test_wave_specialised_kernel_exact(case):
-    """The wave-specialised MFMA kernel (score waves + select waves coupled by
-    LDS counters) returns the oracle's sets, like the default kernel."""
-    if case == "compaction":        # 24 key tiles per row, compactions while tiles stream in
+@pytest.mark.parametrize("case", ["compaction", "ragged", "kvlen_batch", "topk_gt_T", "many_items",
+                                  "long_cand_list"])
+def test_mfma_paths_exact(case):
+    """The MFMA prefill kernel returns the oracle's sets on every path of its
+    candidate lists: default capacity and the smallest one (CSA_CAND_CAP=1:
+    compactions on almost every tile), several query blocks per workgroup,
+    and lists longer than the final select's registers (k = 2200)."""
+    if case == "compaction":        # 24 key tiles per row
         p = _integer_bf16(S_q=96, T=2000, topk=100, q_pos0=6000, qr=1, wr=1, seed=5)
     elif case == "ragged":
         p = _integer_bf16(S_q=37, T=150, topk=20, q_pos0=3)
@@ -195,15 +198,15 @@ def test_wave_specialised_kernel_exact(case):
         p["kv_len"] = np.array([300, 17, 0], dtype=np.int32)
     elif case == "topk_gt_T":
         p = _integer_bf16(S_q=64, T=100, topk=256, q_pos0=1000)
-    else:                           # more query blocks than workgroups: several items per workgroup
-        p = _integer_bf16(S_q=1200, T=700, topk=50, q_pos0=2000, seed=8)
-    _say(f"wave-specialised kernel: {case}")
+    elif case == "many_items":      # 300 query blocks over at most 512 workgroups, light and heavy ones
+        p = _integer_bf16(S_q=1200, T=700, topk=50, q_pos0=0, seed=8)
+    else:                           # k=2200: candidate lists of up to 4464 keys
+        p = _integer_bf16(S_q=8, T=6000, topk=2200, q_pos0=4 * 5990, seed=9)
+    _say(f"mfma prefill paths: {case}")
     ref_i, ref_s, _ = oracle.oracle_topk(p)
-    with _Env(CSA_PREFILL_KERNEL="ws"):
-        idx, sc = _run(p, return_scores=True)
-        idx2, _ = _run(p)
-        with _Env(CSA_CAND_CAP="1"):
-            idx3, _ = _run(p)
-    check_exact(idx, ref_i, sc, ref_s)
-    check_exact(idx2, ref_i)
-    check_exact(idx3, ref_i)
+    for env in ({}, {"CSA_CAND_CAP": "1"}):
+        with _Env(**env):
+            idx, sc = _run(p, return_scores=True)
+            idx2, _ = _run(p)
+        check_exact(idx, ref_i, sc, ref_s)
+        check_exact(idx2, ref_i)
