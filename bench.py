@@ -14,7 +14,7 @@ Also reported on the same JSON line:
                 peak, K rotated over 4 copies so the 256 MB MALL cannot hold it;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50]
 """
 import argparse
 import ctypes
@@ -187,8 +187,9 @@ def cpu_baseline(seconds, R):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed calls first; the GPU clock needs a few tens of ms of load to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only-decode", action="store_true")
