@@ -693,11 +693,17 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
   if (vis <= DEC_REG * DEC_SEL_THREADS) {
     u64 x[DEC_REG];
     const int e0 = wv * (DEC_REG * WAVE) + l;
+    const int last = vis > 0 ? vis - 1 : 0;
+    float v[DEC_REG];
+#pragma unroll
+    for (int j = 0; j < DEC_REG; ++j) {               // every load in flight at once
+      const int s = e0 + j * WAVE;
+      v[j] = sc[s < vis ? s : last];
+    }
 #pragma unroll
     for (int j = 0; j < DEC_REG; ++j) {
       const int s = e0 + j * WAVE;
-      const float v = sc[s < vis ? s : (vis > 0 ? vis - 1 : 0)];
-      x[j] = s < vis ? make_key(v, (uint32_t)s) : 0ull;
+      x[j] = s < vis ? make_key(v[j], (uint32_t)s) : 0ull;
     }
     const u64 T = vis > a.kk ? block_select_kth_regs<DEC_SEL_THREADS, DEC_REG>(x, vis, a.kk, hist, red, list, &lcnt)
                              : 1ull;
