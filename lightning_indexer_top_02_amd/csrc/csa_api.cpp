@@ -116,16 +116,18 @@ PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, ui
 bool decode_fast(const csa_problem* p) { return use_mfma(p) && p->S_q <= CSA_MAX_DECODE_SQ; }
 
 struct DecodePlan {
-  int nsplit;
-  size_t score_bytes, sort_bytes, total;
+  int nsplit, nbw;
+  size_t score_bytes, bound_bytes, sort_bytes, total;
 };
 
 DecodePlan plan_decode(const csa_problem* p, int kk, uint32_t flags) {
   DecodePlan d;
   d.nsplit = (p->T + csa::DEC_CHUNK - 1) / csa::DEC_CHUNK;
+  d.nbw = d.nsplit * (csa::DEC_THREADS / 64);
   d.score_bytes = align_up((size_t)p->B * p->S_q * (p->T + csa::DEC_PAD) * sizeof(float));
+  d.bound_bytes = align_up((size_t)p->B * p->S_q * d.nbw * sizeof(uint4));
   d.sort_bytes = (flags & CSA_SORTED) ? align_up((size_t)p->B * p->S_q * kk * sizeof(float)) : 0;
-  d.total = d.score_bytes + d.sort_bytes;
+  d.total = d.score_bytes + d.bound_bytes + d.sort_bytes;
   return d;
 }
 
@@ -266,12 +268,14 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
     if (ws_bytes < d.total || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, d.total);
     const bool sorted = (flags & CSA_SORTED) != 0;
     float* score_dst = out_score;
-    if (sorted && !score_dst) score_dst = (float*)((char*)ws + d.score_bytes);
+    if (sorted && !score_dst) score_dst = (float*)((char*)ws + d.score_bytes + d.bound_bytes);
     csa::DecodeArgs a{};
     a.q = prob->q; a.k = prob->k; a.w = prob->w; a.kv_len = prob->kv_len;
     a.B = prob->B; a.S_q = prob->S_q; a.T = prob->T; a.m = prob->m; a.q_pos0 = prob->q_pos0;
     a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
     a.scores = (float*)ws;
+    a.bounds = (uint4*)((char*)ws + d.score_bytes);
+    a.nbw = d.nbw;
     a.kk = topk;
     a.out_idx = out_idx;
     a.out_score = score_dst;

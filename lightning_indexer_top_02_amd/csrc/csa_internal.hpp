@@ -50,6 +50,8 @@ struct DecodeArgs {
   long long q_pos0;
   int causal;
   float* scores;        // [B*S_q][T + DEC_PAD] fp32 workspace
+  uint4* bounds;        // [B*S_q][nbw] per-wave selection bounds {order bits, count, max order bits, 0}
+  int nbw;              // bounds per row: DEC_THREADS / WAVE per key chunk
   int kk;
   int32_t* out_idx;
   float* out_score;

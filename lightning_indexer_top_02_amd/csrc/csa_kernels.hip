@@ -668,64 +668,239 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs
     const int s = base0 + st * STRIDE + (l & 31);
     out[s < end ? s : a.T + (l & 31)] = sc[st];       // lanes l and l^32 store the same value
   }
+  // Selection bound of this wave for decode_select_kernel: order bits P and a
+  // count c such that at least c of the wave's keys have order bits >= P.  The
+  // row's k is spread over the waves of its whole chunks as a target g per
+  // wave (so the counts of those waves alone reach k); P is the largest value
+  // with g of the lanes' two best scores at or above it, settled one bit at a
+  // time from ballot counts.  A wave that cannot vouch for g keys that way
+  // (a partial chunk, or g above two keys per lane) reports its smallest
+  // score and all of its keys.
+  {
+    constexpr u64 LO = 0xFFFFFFFFull;                  // lanes 32-63 repeat lanes 0-31
+    constexpr int WPC = DEC_THREADS / WAVE;            // waves per chunk
+    const int nfull = vis / DEC_CHUNK * WPC;           // waves with all DEC_CHUNK / WPC keys
+    const int g = nfull > 0 ? (a.kk + nfull - 1) / nfull : 0x7FFFFFFF;
+    uint32_t t1 = 0u, t2 = 0u, mn = ~0u;               // 0 is below every score's order bits
+    int nv = 0;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const bool ok = base0 + st * STRIDE + (l & 31) < end;
+      const uint32_t o = ok ? score_order_bits(sc[st]) : 0u;
+      t2 = max(t2, min(t1, o));
+      t1 = max(t1, o);
+      mn = ok ? min(mn, o) : mn;
+      nv += __popcll(ballot(ok) & LO);
+    }
+    auto count_ge = [&](uint32_t c) { return __popcll(ballot(t1 >= c) & LO) + __popcll(ballot(t2 >= c) & LO); };
+    uint32_t P = ~0u;
+    int c = 0;
+    if (g <= 64 && count_ge(1u) >= g) {
+      P = 0u;
+      for (int bit = 31; bit >= 16; --bit)            // 16 bits: within 1/128 of the exact value
+        if (count_ge(P | (1u << bit)) >= g) P |= 1u << bit;
+      c = count_ge(P);
+    } else if (nv > 0) {
+      P = wave_min_u32(mn);
+      c = nv;
+    }
+    const uint32_t mx = wave_max_u32(t1);
+    if (l == 0) a.bounds[(size_t)row * a.nbw + blockIdx.x * WPC + wv] = make_uint4(P, (uint32_t)c, mx, 0u);
+  }
 }
 
 // decode_select: one workgroup per query row; exact top-kk of the row's
 // dense scores.  Wave w holds the contiguous element range [w*2048, w*2048+2048)
-// in registers (element w*2048 + j*64 + lane in x[j]), so the emit needs one
-// exchange of per-wave counts and keeps element order (deterministic output).
+// in registers (element w*2048 + j*64 + lane in v[j]).
+//
+// The scan's per-wave bounds give L = min_w P_w with at least sum_w c_w >= kk
+// keys at or above it, so the kk-th largest key scores >= L and only keys
+// scoring >= L (about a tenth of a row of i.i.d. scores) are candidates.  One
+// pass over the registers packs each wave's candidates, in element order, into
+// the wave's LDS segment (the register passes cost VALU time on one CU for
+// every element, so there is only one).  The candidates are histogrammed; keys
+// in bins above the one holding rank kk are emitted in segment order, and the
+// keys of that bin, gathered into an LDS list, are ranked against each other
+// (one thread per key) and the best r emitted in rank order: deterministic
+// output with four block barriers.  Rows the bounds cannot narrow (no bound,
+// equal scores, a full segment, a crowded bin) and rows longer than the
+// registers hold take the select over the dense scores in memory.
 constexpr int DEC_REG = 32;                              // keys per lane: rows up to 32768 in registers
+constexpr int DEC_LIST = 256;                            // boundary-bin keys ranked directly
+constexpr int DEC_SEG = 512;                             // candidate slots per wave (of its 2048 elements)
+
+// Bins for candidate keys whose scores lie in [lo, hi]: on the score's order
+// bits (a fixed number of bins per binade, so a few far outliers at the top do
+// not crowd the bulk near lo into one bin) when the candidates are positive
+// and span at most 20 binades, else linear in the score (finer near lo once
+// the order-bit bins would each cover a large part of a binade).  Both are
+// monotone in the key.
+struct RowBins {
+  bool ord;
+  uint32_t base;
+  int shift;
+  LinBins lin;
+  __device__ __forceinline__ int operator()(u64 key) const {
+    if (ord) {
+      const uint32_t b = ((uint32_t)(key >> 32) - base) >> shift;
+      return (int)(b < (uint32_t)(SEL_BINS - 1) ? b : (uint32_t)(SEL_BINS - 1));
+    }
+    return lin(key);
+  }
+};
+
+__device__ __forceinline__ bool row_bins_ok(uint32_t lo_bits, uint32_t hi_bits, RowBins& rb) {
+  const float lo = order_bits_score(lo_bits), hi = order_bits_score(hi_bits);
+  rb.ord = lo > 0.f && hi < 1048576.f * lo;
+  rb.base = lo_bits;
+  const uint32_t span = hi_bits - lo_bits;
+  const int bits = span ? 32 - __clz((int)span) : 0;
+  rb.shift = bits > SEL_RB ? bits - SEL_RB : 0;
+  if (rb.ord) return span != 0u;
+  return lin_bins_ok(lo, hi, rb.lin);
+}
 
 __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[SEL_BINS];
-  __shared__ u64 red[2 * DEC_SEL_THREADS / WAVE];
-  __shared__ u64 list[BLOCK_LIST];
-  __shared__ int wcnt[DEC_SEL_THREADS / WAVE];
-  __shared__ int lcnt;
   constexpr int NW = DEC_SEL_THREADS / WAVE;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[SEL_BINS];
+  __shared__ u64 red[2 * NW];
+  __shared__ u64 list[DEC_LIST];
+  __shared__ u64 seg_all[NW * DEC_SEG];
+  __shared__ uint32_t part[3 * NW];
+  __shared__ int wcnt[NW];
+  __shared__ int lcnt;
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.x, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
   const float* sc = a.scores + (size_t)row * (a.T + DEC_PAD);
   int32_t* oi = a.out_idx + (size_t)row * a.kk;
   float* os = a.out_score ? a.out_score + (size_t)row * a.kk : nullptr;
+  u64* seg = seg_all + wv * DEC_SEG;
   int w = 0;
-  if (vis <= DEC_REG * DEC_SEL_THREADS) {
-    u64 x[DEC_REG];
+  bool dense = vis > DEC_REG * DEC_SEL_THREADS;
+  if (!dense) {
     const int e0 = wv * (DEC_REG * WAVE) + l;
     const int last = vis > 0 ? vis - 1 : 0;
+    // the row's bounds first: loads complete in order, so reducing them does
+    // not wait for the score loads behind them
+    const int nwr = (vis + DEC_CHUNK - 1) / DEC_CHUNK * (DEC_THREADS / WAVE);   // <= 128 here
+    const uint4 bd = tid < nwr && vis > a.kk ? a.bounds[(size_t)row * a.nbw + tid] : make_uint4(~0u, 0u, 0u, 0u);
     float v[DEC_REG];
 #pragma unroll
     for (int j = 0; j < DEC_REG; ++j) {               // every load in flight at once
       const int s = e0 + j * WAVE;
       v[j] = sc[s < vis ? s : last];
     }
+    if (vis <= a.kk) {                                // every visible key, in element order
+      int mine = 0;
 #pragma unroll
-    for (int j = 0; j < DEC_REG; ++j) {
-      const int s = e0 + j * WAVE;
-      x[j] = s < vis ? make_key(v[j], (uint32_t)s) : 0ull;
+      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(e0 + j * WAVE < vis));
+      if (l == 0) wcnt[wv] = mine;
+      __syncthreads();
+      int off = 0;
+      for (int j = 0; j < wv; ++j) off += wcnt[j];
+#pragma unroll
+      for (int j = 0; j < DEC_REG; ++j) {
+        const int s = e0 + j * WAVE;
+        const u64 m = ballot(s < vis);
+        if (s < vis) emit_key(make_key(v[j], (uint32_t)s), off + lanes_below(m), a.kk, oi, os);
+        off += __popcll(m);
+      }
+      w = vis;
+    } else {
+      // [1] bounds -> L (order bits), their count, row max; clear the histogram meanwhile
+      const uint32_t P0 = wave_min_u32(bd.y ? bd.x : ~0u);
+      const int c0 = wave_sum_i32((int)bd.y);
+      const uint32_t M0 = wave_max_u32(bd.z);
+      if (l == 0) { part[wv] = P0; part[NW + wv] = (uint32_t)c0; part[2 * NW + wv] = M0; }
+      for (int e = 4 * tid; e < SEL_BINS; e += 4 * DEC_SEL_THREADS) *(uint4*)&hist[e] = make_uint4(0u, 0u, 0u, 0u);
+      if (tid == 0) lcnt = 0;
+      __syncthreads();
+      uint32_t P = ~0u, M = 0u;
+      long long cs = 0;
+      for (int j = 0; j < NW; ++j) {
+        P = min(P, part[j]);
+        cs += part[NW + j];
+        M = max(M, part[2 * NW + j]);
+      }
+      RowBins rb;
+      const float lf = order_bits_score(P);
+      bool fast = cs >= a.kk && row_bins_ok(P, M, rb);
+      int cw = 0, bin = 0, r = 0;
+      if (fast) {
+        // [2] the one register pass: pack candidates (score >= L; the float
+        // compare agrees with the order bits, -0 included) into this wave's
+        // segment, then histogram the segment
+#pragma unroll
+        for (int j = 0; j < DEC_REG; ++j) {
+          const int s = e0 + j * WAVE;
+          const bool c = s < vis && v[j] >= lf;
+          const u64 m = ballot(c);
+          const int pos = cw + lanes_below(m);
+          if (c && pos < DEC_SEG) seg[pos] = make_key(v[j], (uint32_t)s);
+          cw += __popcll(m);
+        }
+        wave_lds_sync();
+        const int cn = cw < DEC_SEG ? cw : DEC_SEG;
+        for (int e = l; e < cn; e += WAVE) atomicAdd(&hist[rb(seg[e])], 1u);
+        if (l == 0) wcnt[wv] = cw;
+        __syncthreads();
+        int mx = 0;
+        for (int j = 0; j < NW; ++j) mx = max(mx, wcnt[j]);
+        fast = mx <= DEC_SEG;
+      }
+      if (fast) {
+        // [3] the bin holding rank kk
+        if (wv == 0) {
+          const BinPick pk = wave_pick_bin(hist, SEL_BINS, a.kk);
+          if (l == 0) { red[0] = (u64)pk.bin; red[1] = (u64)pk.above; red[2] = (u64)pk.count; }
+        }
+        __syncthreads();
+        bin = (int)red[0];
+        r = a.kk - (int)red[1];
+        const int bcnt = (int)red[2];
+        fast = bcnt > 0 && bcnt <= DEC_LIST;
+      }
+      if (fast) {
+        // [4] gather the boundary bin; count this wave's keys above it
+        int up = 0;
+        for (int e00 = 0; e00 < cw; e00 += WAVE) {
+          const int e = e00 + l;
+          const u64 x = e < cw ? seg[e] : 0ull;
+          const int bx = e < cw ? rb(x) : -1;
+          up += __popcll(ballot(bx > bin));
+          if (bx == bin) list[atomicAdd(&lcnt, 1)] = x;
+        }
+        if (l == 0) red[4 + wv] = (u64)up;
+        __syncthreads();
+        // [5] keys above the bin, in segment order ...
+        int off = 0;
+        for (int j = 0; j < wv; ++j) off += (int)red[4 + j];
+        for (int e00 = 0; e00 < cw; e00 += WAVE) {
+          const int e = e00 + l;
+          const u64 x = e < cw ? seg[e] : 0ull;
+          const bool keep = e < cw && rb(x) > bin;
+          const u64 m = ballot(keep);
+          if (keep) emit_key(x, off + lanes_below(m), a.kk, oi, os);
+          off += __popcll(m);
+        }
+        // ... and the bin's best r, each placed by its rank within the bin
+        const int bc = lcnt, above = a.kk - r;
+        if (tid < bc) {
+          const u64 x = list[tid];
+          int g = 0;
+#pragma unroll 8
+          for (int q = 0; q < bc; ++q) g += list[q] > x ? 1 : 0;
+          if (g < r) emit_key(x, above + g, a.kk, oi, os);
+        }
+        w = a.kk;
+      } else {
+        dense = true;
+      }
     }
-    const u64 T = vis > a.kk ? block_select_kth_regs<DEC_SEL_THREADS, DEC_REG>(x, vis, a.kk, hist, red, list, &lcnt)
-                             : 1ull;
-    int mine = 0;
-#pragma unroll
-    for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(x[j] >= T));
-    if (l == 0) wcnt[wv] = mine;
+  }
+  if (dense) {                                        // uniform: every decision above came from LDS
     __syncthreads();
-    int off = 0, tot = 0;
-    for (int j = 0; j < NW; ++j) {
-      off += j < wv ? wcnt[j] : 0;
-      tot += wcnt[j];
-    }
-#pragma unroll
-    for (int j = 0; j < DEC_REG; ++j) {
-      const bool keep = x[j] >= T;
-      const u64 m = ballot(keep);
-      if (keep) emit_key(x[j], off + lanes_below(m), a.kk, oi, os);
-      off += __popcll(m);
-    }
-    w = tot;
-  } else {
     const u64 T = block_select_kth_dense<DEC_SEL_THREADS>(sc, vis, a.kk, hist, red);
     for (int base = 0; base < vis; base += DEC_SEL_THREADS) {
       const int s = base + tid;

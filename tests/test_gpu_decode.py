@@ -84,3 +84,61 @@ def test_decode_exact_cases(case):
     check_exact(idx, ref_i, sc, ref_s)
     if case == "sorted":
         assert (idx == ref_i).all() and (sc == ref_s).all()
+
+
+def _bf16_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _select_case(case):
+    """Decode inputs that steer the per-row select down each of its paths."""
+    if case == "no_planted":          # i.i.d. scores: narrow candidate range, tiny boundary bins
+        return csa_inputs.make_decode(B=3, context=131072, topk=2048, n_planted=0, seed=51)
+    if case == "long_rows":           # more visible keys than the select holds in registers
+        return csa_inputs.make_decode(B=2, context=4 * 40000, topk=2048, n_planted=16, seed=52)
+    if case == "ragged_kv":           # partial last chunks, waves without keys, a row below topk
+        p = csa_inputs.make_decode(B=4, context=4 * 9000, topk=1024, n_planted=8, S_q=2, seed=53)
+        p["kv_len"] = np.array([4096 + 40, 1030, 900, 9000], dtype=np.int32)
+        return p
+    if case == "k_near_vis":          # topk close to the row length: waves report all their keys
+        return csa_inputs.make_decode(B=2, context=4 * 3000, topk=2048, n_planted=8, seed=54)
+    if case == "crowded_bin":         # all keys equal but one far above: one bin holds the rest
+        p = csa_inputs.make_decode(B=2, context=4 * 20000, topk=1024, n_planted=1, seed=55)
+        k = _bf16_to_f32(p["k"])
+        for b in range(p["B"]):
+            s = int(p["planted"][b, 0])
+            top = 25.0 * k[b, s]
+            k[b] = k[b, (s + 1) % p["T"]]
+            k[b, s] = top
+        p["k"] = csa_inputs.f32_to_bf16_bits(k)
+        return p
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["no_planted", "long_rows", "ragged_kv", "k_near_vis", "crowded_bin"])
+def test_decode_select_paths(case):
+    p = _select_case(case)
+    _say(f"decode select path case {case}: B={p['B']} S_q={p['S_q']} T={p['T']} k={p['topk']}")
+    idx, sc = _decode(p, return_scores=True)
+    check_tolerance(p, np.arange(p["S_q"]), idx, sc, p["topk"])
+    ref = _prefill(p)
+    for b in range(p["B"]):
+        for r in range(p["S_q"]):
+            assert sorted(idx[b, r].tolist()) == sorted(ref[b, r].tolist()), f"row ({b},{r}) differs from prefill"
+    if case == "crowded_bin":         # ties among the rest: the lowest indices win
+        for b in range(p["B"]):
+            s = int(p["planted"][b, 0])
+            want = [s] + [j for j in range(p["topk"]) if j != s][: p["topk"] - 1]
+            assert sorted(idx[b, 0].tolist()) == sorted(want)
+            assert (sc[b, 0] == sc[b, 0][idx[b, 0] != s][0]).sum() == p["topk"] - 1
+
+
+def test_decode_all_scores_equal():
+    """Every key identical: all scores tie, so the lowest indices win."""
+    p = csa_inputs.make_decode(B=2, context=4 * 5000, topk=300, n_planted=0, seed=56)
+    p["k"] = np.ascontiguousarray(np.repeat(p["k"][:, :1, :], p["T"], axis=1))
+    _say("decode all-equal scores")
+    idx, sc = _decode(p, return_scores=True)
+    for b in range(p["B"]):
+        assert sorted(idx[b, 0].tolist()) == list(range(p["topk"]))
+        assert (sc[b, 0] == sc[b, 0, 0]).all()
