@@ -59,6 +59,7 @@ struct DecodeArgs {
 
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_CHUNK = 1024;        // keys per decode-scan workgroup
+constexpr int DEC_RING = 3;            // key-row buffers per wave in the decode scan
 constexpr int DEC_PAD = 64;            // floats after each score row (stores of keys past the end)
 constexpr int DEC_SEL_THREADS = 1024;
 

@@ -608,19 +608,11 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs
   if (start >= end) return;
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
-
-  bf16x8 A[2][8];
-  float wl[2][16];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const bf16x8* src = (const bf16x8*)(Q + ((size_t)row * MH + rt * 32 + (l & 31)) * MD);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) wl[rt][e] = a.w[(size_t)row * MH + rt * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3)];
-  }
-  // Each wave takes 32-key steps round-robin; the next step's key rows are
-  // requested before the current step's MFMAs so ~8 KB per wave is in flight.
+  // The query's 64x128 A operand lives in LDS in MFMA lane order (each wave
+  // copies two of the eight 16-deep slices; 16-byte reads without bank
+  // conflicts), which leaves the registers for a ring of DEC_RING key-row
+  // buffers: DEC_RING - 1 steps (8 KB each per wave) stay in flight.
+  __shared__ bf16x8 Als[2][8][WAVE];
   float* out = a.scores + (size_t)row * (a.T + DEC_PAD);
   const size_t kseq = (size_t)b * a.T;
   constexpr int STEP = 32, STRIDE = STEP * (DEC_THREADS / WAVE);
@@ -631,37 +623,50 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) bf[kk] = src[2 * kk + (l >> 5)];
   };
-  // one step on the key rows in `cur` while the next step's rows load into `nxt`
-  auto step = [&](int base, bf16x8 (&cur)[8], bf16x8 (&nxt)[8]) -> float {
-    load(base + STRIDE, nxt);                         // unconditional: rows past `end` are clamped
+  static_assert(DEC_CHUNK % STRIDE == 0, "decode chunk must be whole steps");
+  static_assert(DEC_THREADS / WAVE * 2 == 8, "each wave copies two query slices");
+  constexpr int NSTEP = DEC_CHUNK / STRIDE;
+  const int base0 = start + STEP * wv;
+  bf16x8 qa[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const bf16x8* src = (const bf16x8*)(Q + ((size_t)row * MH + rt * 32 + (l & 31)) * MD);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qa[rt][h] = src[2 * (2 * wv + h) + (l >> 5)];
+  }
+  bf16x8 bb[DEC_RING][8];
+#pragma unroll
+  for (int st = 0; st < DEC_RING - 1; ++st) load(base0 + st * STRIDE, bb[st]);
+  float wl[2][16];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) wl[rt][e] = a.w[(size_t)row * MH + rt * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3)];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) Als[rt][2 * wv + h][l] = qa[rt][h];
+  __syncthreads();
+  // Steps are a compile-time count, so the loop unrolls completely: a ring of
+  // DEC_RING buffers without register copies, and exact wait counts for the
+  // prefetched rows because scores stay in registers until the loop ends.
+  float sc[NSTEP];
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    if (st + DEC_RING - 1 < NSTEP) load(base0 + (st + DEC_RING - 1) * STRIDE, bb[(st + DEC_RING - 1) % DEC_RING]);
+    asm volatile("" ::: "memory");                    // re-read the A slices from LDS every step
     __builtin_amdgcn_sched_barrier(0);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], cur[kk], acc[rt], 0, 0, 0);
+      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Als[rt][kk][l], bb[st % DEC_RING][kk], acc[rt], 0, 0, 0);
     float ps = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) ps = __builtin_fmaf(wl[rt][e], relu(acc[rt][e]), ps);
-    return half_swap_sum(ps, ps);                     // both halves: the full score of key (l & 31)
-  };
-  // The chunk is a compile-time DEC_CHUNK keys (DEC_CHUNK / STRIDE steps per
-  // wave), so the step loop unrolls completely: ping-pong buffers without
-  // register copies and exact wait counts for the prefetched rows.
-  // Scores stay in registers until the loop ends: with only loads inside it,
-  // the compiler's wait counts for the prefetched rows are exact.
-  static_assert(DEC_CHUNK % STRIDE == 0, "decode chunk must be whole steps");
-  constexpr int NSTEP = DEC_CHUNK / STRIDE;
-  bf16x8 b0[8], b1[8];
-  float sc[NSTEP];
-  const int base0 = start + STEP * wv;
-  load(base0, b0);
-#pragma unroll
-  for (int st = 0; st < NSTEP; st += 2) {
-    sc[st] = step(base0 + st * STRIDE, b0, b1);
-    if (st + 1 < NSTEP) sc[st + 1] = step(base0 + (st + 1) * STRIDE, b1, b0);
+    sc[st] = half_swap_sum(ps, ps);                   // both halves: the full score of key (l & 31)
   }
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st) {               // no branch: keys past the end go to the row's pad
