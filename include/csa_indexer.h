@@ -37,8 +37,9 @@
  *    out_score (optional, may be NULL) holds the fp32 score of each entry and
  *    -INFINITY for padding.
  *  - Workspace: `ws` must hold at least csa_workspace_size(...) bytes for the
- *    same problem, flags and device; it needs no initialisation and its
- *    contents are undefined after the call.  ws may be NULL when that size is 0.
+ *    same problem, flags and device and be 16-byte aligned (CSA_ERR_INVALID
+ *    otherwise); it needs no initialisation and its contents are undefined
+ *    after the call.  ws may be NULL when that size is 0.
  *  - Calls that share a workspace must not overlap (same stream = safe).
  */
 #ifndef CSA_INDEXER_H

@@ -156,6 +156,7 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
   const PrefillPlan pl = plan_prefill(p, kk, P, out_stride, flags);
   if (ws_bytes < pl.total || (pl.total > 0 && !ws))
     return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, pl.total);
+  if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
   const bool mfma = use_mfma(p);
   const bool sorted = (flags & CSA_SORTED) != 0;
   float* score_dst = out_score;
@@ -266,6 +267,7 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
                                 ws_bytes, hip_stream);
     const DecodePlan d = plan_decode(prob, topk, flags);
     if (ws_bytes < d.total || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, d.total);
+    if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
     const bool sorted = (flags & CSA_SORTED) != 0;
     float* score_dst = out_score;
     if (sorted && !score_dst) score_dst = (float*)((char*)ws + d.score_bytes + d.bound_bytes);

@@ -770,7 +770,8 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
   __shared__ __attribute__((aligned(16))) uint32_t hist[SEL_BINS];
   __shared__ u64 red[2 * NW];
   __shared__ u64 list[DEC_LIST];
-  __shared__ u64 seg_all[NW * DEC_SEG];
+  __shared__ float segv_all[NW * DEC_SEG];            // candidate scores and indices, per wave
+  __shared__ uint32_t segi_all[NW * DEC_SEG];
   __shared__ uint32_t part[3 * NW];
   __shared__ int wcnt[NW];
   __shared__ int lcnt;
@@ -780,7 +781,9 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
   const float* sc = a.scores + (size_t)row * (a.T + DEC_PAD);
   int32_t* oi = a.out_idx + (size_t)row * a.kk;
   float* os = a.out_score ? a.out_score + (size_t)row * a.kk : nullptr;
-  u64* seg = seg_all + wv * DEC_SEG;
+  float* segv = segv_all + wv * DEC_SEG;
+  uint32_t* segi = segi_all + wv * DEC_SEG;
+  auto seg = [&](int e) { return make_key(segv[e], segi[e]); };
   int w = 0;
   bool dense = vis > DEC_REG * DEC_SEL_THREADS;
   if (!dense) {
@@ -836,18 +839,24 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
         // [2] the one register pass: pack candidates (score >= L; the float
         // compare agrees with the order bits, -0 included) into this wave's
         // segment, then histogram the segment
+        // (score and index as two 32-bit words: no key is formed per element,
+        // and a wave whose whole range is visible skips the range test)
+        auto pack = [&](auto in_range) {
 #pragma unroll
-        for (int j = 0; j < DEC_REG; ++j) {
-          const int s = e0 + j * WAVE;
-          const bool c = s < vis && v[j] >= lf;
-          const u64 m = ballot(c);
-          const int pos = cw + lanes_below(m);
-          if (c && pos < DEC_SEG) seg[pos] = make_key(v[j], (uint32_t)s);
-          cw += __popcll(m);
-        }
+          for (int j = 0; j < DEC_REG; ++j) {
+            const int s = e0 + j * WAVE;
+            const bool c = in_range(s) && v[j] >= lf;
+            const u64 m = ballot(c);
+            const int pos = cw + lanes_below(m);
+            if (c && pos < DEC_SEG) { segv[pos] = v[j]; segi[pos] = (uint32_t)s; }
+            cw += __popcll(m);
+          }
+        };
+        if ((wv + 1) * DEC_REG * WAVE <= vis) pack([](int) { return true; });
+        else pack([&](int s) { return s < vis; });
         wave_lds_sync();
         const int cn = cw < DEC_SEG ? cw : DEC_SEG;
-        for (int e = l; e < cn; e += WAVE) atomicAdd(&hist[rb(seg[e])], 1u);
+        for (int e = l; e < cn; e += WAVE) atomicAdd(&hist[rb(seg(e))], 1u);
         if (l == 0) wcnt[wv] = cw;
         __syncthreads();
         int mx = 0;
@@ -871,7 +880,7 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
         int up = 0;
         for (int e00 = 0; e00 < cw; e00 += WAVE) {
           const int e = e00 + l;
-          const u64 x = e < cw ? seg[e] : 0ull;
+          const u64 x = e < cw ? seg(e) : 0ull;
           const int bx = e < cw ? rb(x) : -1;
           up += __popcll(ballot(bx > bin));
           if (bx == bin) list[atomicAdd(&lcnt, 1)] = x;
@@ -883,7 +892,7 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
         for (int j = 0; j < wv; ++j) off += (int)red[4 + j];
         for (int e00 = 0; e00 < cw; e00 += WAVE) {
           const int e = e00 + l;
-          const u64 x = e < cw ? seg[e] : 0ull;
+          const u64 x = e < cw ? seg(e) : 0ull;
           const bool keep = e < cw && rb(x) > bin;
           const u64 m = ballot(keep);
           if (keep) emit_key(x, off + lanes_below(m), a.kk, oi, os);

@@ -98,6 +98,8 @@ def test_other_argument_errors(lib):
     assert _call_prefill(lib, p, out=None) == Bd.CSA_ERR_INVALID
     # workspace too small -> rejected before anything is enqueued
     assert _call_prefill(lib, p, ws=0x5000, ws_bytes=16) == Bd.CSA_ERR_WORKSPACE
+    # workspace not 16-byte aligned -> rejected before anything is enqueued
+    assert _call_prefill(lib, p, ws=0x5004, ws_bytes=1 << 40) == Bd.CSA_ERR_INVALID
     # decode: too many query rows
     p2 = _prob(S_q=17)
     assert lib.csa_index_topk_decode(ctypes.byref(p2), 16, 0, 0x4000, None, None, 0, None) == Bd.CSA_ERR_UNSUPPORTED
