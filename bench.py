@@ -9,7 +9,8 @@ per (query, visible key) pair over rows with more visible keys than k.
 
 Also reported on the same JSON line:
   roofline      the prefill kernel against the bf16 MFMA peak (HIP-event time
-                of each launch on the library's stream);
+                of each launch on the library's stream, in a pass of its own
+                after the timed region);
   decode        the decode scan (B=32 x T=32768, k=2048) in GB/s against HBM
                 peak, K rotated over 4 copies so the 256 MB MALL cannot hold it;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
@@ -45,23 +46,29 @@ def _to_dev(p, torch, dev):
 
 
 def _time_calls(torch, call, steps, warmup):
-    """Warm up, then time `steps` calls with HIP events on the current stream."""
+    """Warm up, then time exactly `steps` back-to-back calls between two HIP
+    events on the current stream (the timed region).  Per-launch durations
+    come from a second pass of `steps` calls, each bracketed by its own event
+    pair: an event recorded between two calls leaves the GPU idle for a few
+    microseconds, so those events stay out of the timed region."""
     for i in range(warmup):
         call(i)
-    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(st)
     for i in range(steps):
-        ev[i][0].record(st)
         call(i)
-        ev[i][1].record(st)
     t1.record(st)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(st)
+        call(i)
+        ev[i][1].record(st)
+    torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in ev)
     return total_ms, sum(per) / len(per), per[len(per) // 2], per[0]
 
