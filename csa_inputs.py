@@ -98,6 +98,24 @@ def make_decode(B=32, context=131072, m=4, H=64, D=128, topk=2048, n_planted=64,
     return prob
 
 
+def make_attention(B, S_q, T, H=64, Dk=128, Dv=128, n_sel=2048, seed=0, pad=0, name=""):
+    """Inputs of the sparse attention step: q [B,S_q,H,Dk], k [B,T,Dk] and
+    v [B,T,Dv] ~ N(0,1) rounded to bf16, and per query row n_sel distinct key
+    indices drawn uniformly from [0, T) with the last `pad` entries set to -1."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(rng.standard_normal((B, S_q, H, Dk), dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, T, Dk), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, T, Dv), dtype=np.float32))
+    idx = np.empty((B, S_q, n_sel), dtype=np.int32)
+    for b in range(B):
+        for t in range(S_q):
+            idx[b, t] = rng.choice(T, size=n_sel, replace=False)
+    if pad:
+        idx[:, :, n_sel - pad:] = -1
+    return dict(B=B, S_q=S_q, T=T, H=H, Dk=Dk, Dv=Dv, n_sel=n_sel, q=q, k=k, v=v, idx=idx,
+                scale=float(1.0 / np.sqrt(Dk)), seed=seed, name=name)
+
+
 # --- the five named workloads -------------------------------------------------
 
 def config(n: int):

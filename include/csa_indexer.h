@@ -3,7 +3,7 @@
  *
  * The operation.  DeepSeek-V3.2/V4 Compressed Sparse Attention (CSA) scores
  * every compressed key with a "lightning indexer" and keeps the top-k keys of
- * each query; a sparse attention kernel then reads only those keys
+ * each query; the attention step that follows touches only the selected keys
  * ("StreamIndex: Memory-Bounded Compressed Sparse Attention via Streaming
  * Top-k", abstract).  The indexer score is a per-head dot product of the query
  * with the compressed key, passed through ReLU and fused across heads with
@@ -106,8 +106,8 @@ typedef struct {
 csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap, int32_t P,
                               uint32_t flags, size_t* bytes);
 
-/* Top-k key indices per query row (StreamIndex abstract: "the top-k are
- * selected per query"), streaming over key tiles with a running per-query
+/* Top-k key indices per query row (StreamIndex abstract: every query keeps
+ * its own top-k keys), streaming over key tiles with a running per-query
  * threshold; any S_q.  out_idx [B, S_q, topk] int32; out_score [B, S_q, topk]
  * fp32 or NULL.  1 <= topk <= CSA_MAX_TOPK. */
 csa_status csa_index_topk_prefill(const csa_problem* prob, int32_t topk, uint32_t flags,

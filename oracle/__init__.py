@@ -9,3 +9,4 @@ from .csa_oracle import (  # noqa: F401
     logit_threshold, exact_int_scores, exhaustive_topk,
     row_score_vector, RowScorer,
 )
+from .csa_attention_oracle import attention_row, oracle_attention  # noqa: F401
