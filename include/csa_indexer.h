@@ -156,6 +156,38 @@ csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref,
                           int64_t rows, int32_t T, float* out_recall, void* ws, size_t ws_bytes,
                           void* hip_stream);
 
+/* Sparse attention over the selected keys: the CSA step that consumes the
+ * indexer's out_idx (StreamIndex abstract: the attention step of CSA reads
+ * only the keys the indexer picks; the Multi-layer Indexer blog post: each
+ * DeepSeek Sparse Attention layer attends to the 2048 entries its indexer
+ * picks).  The pages give no formula for this step; it is read as scaled
+ * softmax attention in which every query head attends to the same selected
+ * compressed key and value rows:
+ *
+ *   o[b,t,h,:] = sum_e p_e v[b, idx[b,t,e], :],
+ *   p = softmax_e( scale * q[b,t,h,:] . k[b, idx[b,t,e], :] )
+ *
+ * over the entries e of idx[b,t,0:n_sel] with 0 <= idx < T (others skipped;
+ * an index listed twice counts twice); a row with no valid entry gives 0.
+ * q [B,S_q,H,Dk], k [B,T,Dk], v [B,T,Dv] bf16; idx [B,S_q,n_sel] int32 (for
+ * example out_idx of a top-k call); out [B,S_q,H,Dv] fp32.  This build:
+ * H = 64, Dk = Dv = 128 (CSA_ERR_UNSUPPORTED otherwise); n_sel >= 1; scale
+ * finite.  Computed in fp32 from bf16 inputs with the softmax weights rounded
+ * to bf16 for the weighted sum of value rows. */
+typedef struct {
+  uint32_t struct_size; /* must equal sizeof(csa_attn_problem) */
+  int32_t B, S_q, T, H, Dk, Dv;
+  const void* q;
+  const void* k;
+  const void* v;
+} csa_attn_problem;
+
+/* Workspace bytes of csa_sparse_attention for this problem and n_sel. */
+csa_status csa_attention_workspace_size(const csa_attn_problem* prob, int32_t n_sel, size_t* bytes);
+
+csa_status csa_sparse_attention(const csa_attn_problem* prob, const int32_t* idx, int32_t n_sel, float scale,
+                                float* out, void* ws, size_t ws_bytes, void* hip_stream);
+
 const char* csa_status_str(csa_status s); /* static string, never NULL */
 const char* csa_last_error(void);         /* thread-local detail of this thread's last error */
 int csa_version(void);                    /* major*10000 + minor*100 + patch */

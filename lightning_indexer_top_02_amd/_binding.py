@@ -9,6 +9,7 @@ enqueued on torch's current stream.  The library must be built
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +42,17 @@ class CsaProblem(ctypes.Structure):
     ]
 
 
+class CsaAttnProblem(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", ctypes.c_int32), ("S_q", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("H", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.POINTER(CsaProblem)
+_PA = ctypes.POINTER(CsaAttnProblem)
 _vp, _i32, _u32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
 
 _SIGS = {
@@ -51,6 +62,8 @@ _SIGS = {
     "csa_index_threshold_select": (_i32, [_P, _f32, _f32, _i32, _u32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_interleaved": (_i32, [_P, _i32, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
     "csa_set_recall": (_i32, [_vp, _i32, _vp, _i32, ctypes.c_int64, _i32, _vp, _vp, _sz, _vp]),
+    "csa_attention_workspace_size": (_i32, [_PA, _i32, ctypes.POINTER(_sz)]),
+    "csa_sparse_attention": (_i32, [_PA, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
     "csa_status_str": (ctypes.c_char_p, [_i32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_version": (ctypes.c_int, []),
@@ -241,3 +254,44 @@ def set_recall(sel, ref, T, out=None):
     _check(load_library().csa_set_recall(_ptr(sel), int(n_sel), _ptr(ref), int(n_ref), int(rows), int(T),
                                          _ptr(rec), None, 0, _stream_handle()))
     return rec
+
+
+def make_attn_problem(q, k, v):
+    """Describe bf16 q [B,S_q,H,Dk], k [B,T,Dk], v [B,T,Dv] (contiguous GPU tensors)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, S_q, H, Dk = q.shape
+    if k.shape[0] != B or v.shape[0] != B or k.shape[1] != v.shape[1] or k.shape[2] != Dk:
+        raise ValueError("shape mismatch between q, k and v")
+    return CsaAttnProblem(ctypes.sizeof(CsaAttnProblem), B, S_q, k.shape[1], H, Dk, v.shape[2],
+                          _ptr(q), _ptr(k), _ptr(v))
+
+
+def attention_workspace_size(prob, n_sel) -> int:
+    n = _sz(0)
+    _check(load_library().csa_attention_workspace_size(ctypes.byref(prob), int(n_sel), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attention(q, k, v, idx, *, scale=None, out=None, workspace=None):
+    """Softmax attention of every head of q [B,S_q,H,Dk] over the key and value
+    rows idx [B,S_q,n_sel] selects (entries outside [0, T) skipped); returns
+    fp32 [B,S_q,H,Dv].  scale defaults to 1/sqrt(Dk)."""
+    torch = _torch()
+    if idx.dtype != torch.int32 or not (idx.is_cuda and idx.is_contiguous()):
+        raise TypeError("idx must be a contiguous int32 GPU tensor")
+    prob = make_attn_problem(q, k, v)
+    n_sel = idx.shape[-1]
+    if idx.numel() != q.shape[0] * q.shape[1] * n_sel:
+        raise ValueError("idx must be [B, S_q, n_sel]")
+    scale = float(1.0 / math.sqrt(q.shape[3])) if scale is None else float(scale)
+    o = out if out is not None else torch.empty((q.shape[0], q.shape[1], q.shape[2], v.shape[2]),
+                                               dtype=torch.float32, device=q.device)
+    ws = _workspace(attention_workspace_size(prob, n_sel), q.device, workspace)
+    _check(load_library().csa_sparse_attention(ctypes.byref(prob), _ptr(idx), int(n_sel), scale, _ptr(o),
+                                               _ptr(ws), _nbytes(ws), _stream_handle()))
+    return o

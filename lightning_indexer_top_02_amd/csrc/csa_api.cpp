@@ -342,6 +342,85 @@ csa_status csa_index_topk_interleaved(const csa_problem* prob, int32_t P, int32_
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+struct AttnPlan {
+  int nsplit;
+  size_t opart_bytes, stat_bytes, total;
+};
+
+// Workgroups per query row: about 256 workgroups in all (the chunk kernel
+// runs one per CU), never more than the row has 128-entry chunks.
+AttnPlan plan_attention(const csa_attn_problem* p, int n_sel) {
+  AttnPlan pl;
+  const long long rows = (long long)p->B * p->S_q;
+  const int nchunk = (n_sel + csa::AT_CHUNK - 1) / csa::AT_CHUNK;
+  long long ns = (256 + rows - 1) / rows;
+  ns = std::max(1ll, std::min(ns, (long long)nchunk));
+  pl.nsplit = (int)ns;
+  pl.opart_bytes = align_up((size_t)rows * pl.nsplit * csa::AT_H * csa::AT_D * sizeof(float));
+  pl.stat_bytes = align_up((size_t)rows * pl.nsplit * csa::AT_H * sizeof(float));
+  pl.total = pl.opart_bytes + 2 * pl.stat_bytes;
+  return pl;
+}
+
+csa_status validate_attention(const csa_attn_problem* p, int n_sel) {
+  if (!p) return fail(CSA_ERR_INVALID, "problem is NULL");
+  if (p->struct_size != sizeof(csa_attn_problem)) return fail(CSA_ERR_INVALID, "struct_size mismatch");
+  if (p->B < 1 || p->S_q < 1 || p->T < 1) return fail(CSA_ERR_INVALID, "B, S_q and T must be >= 1");
+  if (n_sel < 1) return fail(CSA_ERR_INVALID, "n_sel=%d < 1", n_sel);
+  if (p->H != csa::AT_H || p->Dk != csa::AT_D || p->Dv != csa::AT_D)
+    return fail(CSA_ERR_UNSUPPORTED, "sparse attention needs H=64, Dk=Dv=128 (got H=%d Dk=%d Dv=%d)", p->H, p->Dk, p->Dv);
+  if (!p->q || !p->k || !p->v) return fail(CSA_ERR_INVALID, "q, k and v must not be NULL");
+  if ((long long)p->B * p->S_q > (1ll << 31) - 1) return fail(CSA_ERR_UNSUPPORTED, "too many query rows");
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status csa_attention_workspace_size(const csa_attn_problem* prob, int32_t n_sel, size_t* bytes) {
+  try {
+    if (!bytes) return fail(CSA_ERR_INVALID, "bytes is NULL");
+    const csa_status s = validate_attention(prob, n_sel);
+    if (s != CSA_OK) return s;
+    *bytes = plan_attention(prob, n_sel).total;
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+csa_status csa_sparse_attention(const csa_attn_problem* prob, const int32_t* idx, int32_t n_sel, float scale,
+                                float* out, void* ws, size_t ws_bytes, void* hip_stream) {
+  try {
+    const csa_status s = validate_attention(prob, n_sel);
+    if (s != CSA_OK) return s;
+    if (!idx || !out) return fail(CSA_ERR_INVALID, "idx and out must not be NULL");
+    if (!std::isfinite(scale)) return fail(CSA_ERR_INVALID, "scale must be finite");
+    const AttnPlan pl = plan_attention(prob, n_sel);
+    if (ws_bytes < pl.total || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, pl.total);
+    if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
+    csa::AttnArgs a{};
+    a.q = prob->q; a.k = prob->k; a.v = prob->v; a.idx = idx;
+    a.B = prob->B; a.S_q = prob->S_q; a.T = prob->T; a.n_sel = n_sel; a.scale = scale;
+    a.nsplit = pl.nsplit;
+    char* wp = (char*)ws;
+    a.opart = (float*)wp;
+    a.mpart = (float*)(wp + pl.opart_bytes);
+    a.lpart = (float*)(wp + pl.opart_bytes + pl.stat_bytes);
+    a.out = out;
+    hipError_t e = csa::launch_attention(a, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "attention launch failed: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
 csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref, int32_t n_ref, int64_t rows,
                           int32_t T, float* out_recall, void* ws, size_t ws_bytes, void* hip_stream) {
   (void)ws;

@@ -63,6 +63,27 @@ constexpr int DEC_RING = 3;            // key-row buffers per wave in the decode
 constexpr int DEC_PAD = 64;            // floats after each score row (stores of keys past the end)
 constexpr int DEC_SEL_THREADS = 1024;
 
+// Sparse attention over selected keys (H = 64 heads, Dk = Dv = 128, bf16).
+constexpr int AT_H = 64, AT_D = 128;
+constexpr int AT_CHUNK = 128;          // selected keys per step of a workgroup
+constexpr int AT_THREADS = 256;
+
+struct AttnArgs {
+  const void* q;        // [rows][AT_H][AT_D] bf16
+  const void* k;        // [B][T][AT_D] bf16
+  const void* v;        // [B][T][AT_D] bf16
+  const int32_t* idx;   // [rows][n_sel]
+  int B, S_q, T, n_sel;
+  float scale;
+  int nsplit;           // workgroups per query row (each takes chunks split, split + nsplit, ...)
+  float* opart;         // [rows][nsplit][AT_H][AT_D] unnormalised partial outputs
+  float* mpart;         // [rows][nsplit][AT_H] running max (-inf: no valid entry)
+  float* lpart;         // [rows][nsplit][AT_H] sum of exp(z - max)
+  float* out;           // [rows][AT_H][AT_D]
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
 // mfma: the bf16 H=64 D=128 MFMA kernel; otherwise the generic kernel for a.bf16.
 hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, hipStream_t st);
 // Resident workgroups per CU of the chosen prefill kernel (>= 1).

@@ -940,6 +940,181 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
   }
 }
 
+// ============================================================ sparse attention
+//
+// CSA stage 4: every query head attends, with scaled softmax, to the key and
+// value rows its row of indices selects (the indexer's output); entries
+// outside [0, T) are skipped.  H = 64 heads, Dk = Dv = 128, bf16 inputs,
+// fp32 accumulation and output.
+//
+// attn_chunk_kernel: grid (nsplit, rows), 4 waves.  A workgroup takes the
+// row's 128-entry chunks split, split + nsplit, ... with an online softmax.
+// Per chunk: wave w gathers the key rows of entries 32w..32w+31 straight into
+// MFMA B operands (16 B per lane) and forms the 64 x 32 logits with the
+// query as the A operand (registers, loaded once); the chunk's per-head max
+// and the running max come through LDS; p = exp(z - m) goes to LDS as bf16 in
+// the MFMA A layout, the chunk's value rows go to LDS transposed (dv-major),
+// and wave w then accumulates output columns 32w..32w+31 of all 64 heads with
+// P.V MFMAs after rescaling them by exp(m_old - m_new).  Both LDS tiles are
+// XOR-swizzled in 16-byte pieces (piece ^ row % 16) so that the 16-byte
+// operand reads of 32 rows at the same piece spread over the banks.
+// attn_combine_kernel merges the nsplit partial results of a row.
+
+__device__ __forceinline__ uint32_t at_swz(int r, int col) {   // bf16 element (r, col) of a 128-wide tile
+  return (uint32_t)(r * AT_CHUNK * 2 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) << 1)));
+}
+
+__global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char ps[AT_H * AT_CHUNK * 2];      // P (bf16), head-major
+  __shared__ __attribute__((aligned(16))) char vt[AT_D * AT_CHUNK * 2];      // V^T (bf16), dv-major
+  __shared__ float red[4][AT_H];
+  __shared__ float mrun[AT_H], lrun[AT_H], mnew_s[AT_H], alpha_s[AT_H];
+  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  const int row = blockIdx.y, split = blockIdx.x, b = row / a.S_q;
+  const int nchunk = (a.n_sel + AT_CHUNK - 1) / AT_CHUNK;
+  const __bf16* K = (const __bf16*)a.k;
+  const __bf16* V = (const __bf16*)a.v;
+  const int32_t* irow = a.idx + (size_t)row * a.n_sel;
+  const size_t kseq = (size_t)b * a.T;
+
+  bf16x8 A[2][8];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)row * AT_H + rt * 32 + (l & 31)) * AT_D);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
+  }
+  if (tid < AT_H) {
+    mrun[tid] = -__builtin_inff();
+    lrun[tid] = 0.f;
+  }
+  f32x16 o[2] = {f32x16{}, f32x16{}};                   // output columns 32w + (l & 31)
+  // head row of accumulator element e (rows of tile rt are rt*32 + this)
+  auto hrow = [&](int e) { return 8 * (e >> 2) + 4 * (l >> 5) + (e & 3); };
+
+  for (int c = split; c < nchunk; c += a.nsplit) {
+    const int j0 = c * AT_CHUNK;
+    // this lane's key column for the logits, and this thread's value row
+    const int jk = j0 + 32 * wv + (l & 31);
+    const int ik = jk < a.n_sel ? irow[jk] : -1;
+    const bool vk = ik >= 0 && ik < a.T;
+    const int jv = j0 + (tid >> 1);
+    const int iv = jv < a.n_sel ? irow[jv] : -1;
+    const bool vv = iv >= 0 && iv < a.T;
+    bf16x8 bk[8], vr[8];
+    {
+      const bf16x8* src = (const bf16x8*)(K + (kseq + (vk ? ik : 0)) * AT_D);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) bk[kk] = src[2 * kk + (l >> 5)];
+    }
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], bk[kk], acc[rt], 0, 0, 0);
+    {                                                   // value rows load while the softmax statistics settle
+      const bf16x8* vsrc = (const bf16x8*)(V + (kseq + (vv ? iv : 0)) * AT_D + (tid & 1) * 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vr[i] = vsrc[i];
+    }
+    // scaled logits; skipped entries at -inf; per-head max over the wave's 32 entries
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = vk ? a.scale * acc[rt][e] : -__builtin_inff();
+        acc[rt][e] = x;                                 // the logit, in place
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, WAVE));
+        if ((l & 31) == 0) red[wv][rt * 32 + hrow(e)] = x;
+      }
+    __syncthreads();
+    if (tid < AT_H) {
+      const float cm = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+      const float mo = mrun[tid], mn = fmaxf(mo, cm);
+      mnew_s[tid] = mn;
+      alpha_s[tid] = mn == -__builtin_inff() ? 1.f : __expf(mo - mn);
+    }
+    __syncthreads();
+    // p = exp(z - m_new) to LDS (bf16, A layout); per-head sums of the wave's p
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int h = rt * 32 + hrow(e);
+        const float mn = mnew_s[h];
+        const float pv = mn == -__builtin_inff() ? 0.f : __expf(acc[rt][e] - mn);
+        const __bf16 pb = (__bf16)pv;
+        *(__bf16*)(ps + at_swz(h, 32 * wv + (l & 31))) = pb;
+        float x = (float)pb;                            // the sum of what the P.V product uses
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, WAVE);
+        if ((l & 31) == 0) red[wv][h] = x;
+      }
+    // value row jv - j0 = tid / 2, columns (tid & 1) * 64 .. + 63, transposed
+    {
+      const int kcol = tid >> 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *(__bf16*)(vt + at_swz((tid & 1) * 64 + 8 * i + e, kcol)) = vr[i][e];
+    }
+    __syncthreads();
+    if (tid < AT_H) {
+      lrun[tid] = alpha_s[tid] * lrun[tid] + (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
+      mrun[tid] = mnew_s[tid];
+    }
+    // rescale this wave's output columns, then O += P . V over the chunk
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[rt][e] *= alpha_s[rt * 32 + hrow(e)];
+#pragma unroll
+    for (int ks = 0; ks < AT_CHUNK / 16; ++ks) {
+      const int kc = 16 * ks + 8 * (l >> 5);
+      const bf16x8 bv = *(const bf16x8*)(vt + at_swz(32 * wv + (l & 31), kc));
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const bf16x8 ap = *(const bf16x8*)(ps + at_swz(rt * 32 + (l & 31), kc));
+        o[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bv, o[rt], 0, 0, 0);
+      }
+    }
+    __syncthreads();                                    // P, V^T and the stats are reused by the next chunk
+  }
+  const size_t pr = (size_t)row * a.nsplit + split;
+  float* op = a.opart + pr * AT_H * AT_D;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) op[(size_t)(rt * 32 + hrow(e)) * AT_D + 32 * wv + (l & 31)] = o[rt][e];
+  if (tid < AT_H) {
+    a.mpart[pr * AT_H + tid] = mrun[tid];
+    a.lpart[pr * AT_H + tid] = lrun[tid];
+  }
+}
+
+// One workgroup per query row: o = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s
+// over the row's partial results (0 where no entry was valid).
+__global__ __launch_bounds__(AT_THREADS) void attn_combine_kernel(AttnArgs a) {
+  const int row = blockIdx.x;
+  const size_t pr0 = (size_t)row * a.nsplit;
+  for (int x = threadIdx.x; x < AT_H * AT_D; x += AT_THREADS) {
+    const int h = x / AT_D;
+    float M = -__builtin_inff();
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.mpart[(pr0 + s) * AT_H + h]);
+    float num = 0.f, den = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int s = 0; s < a.nsplit; ++s) {
+        const float ms = a.mpart[(pr0 + s) * AT_H + h];
+        const float f = ms == -__builtin_inff() ? 0.f : __expf(ms - M);
+        num += f * a.opart[(pr0 + s) * AT_H * AT_D + x];
+        den += f * a.lpart[(pr0 + s) * AT_H + h];
+      }
+    }
+    a.out[(size_t)row * AT_H * AT_D + x] = den > 0.f ? num / den : 0.f;
+  }
+}
+
 // ============================================================ row sort
 //
 // Sorts each row of `len` (index, score) pairs by (score desc, index asc);
@@ -1103,6 +1278,16 @@ hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_select_kernel<<<a.B * a.S_q, DEC_SEL_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+  const long long rows = (long long)a.B * a.S_q;
+  if (rows <= 0) return hipSuccess;
+  attn_chunk_kernel<<<dim3(a.nsplit, (unsigned)rows), AT_THREADS, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine_kernel<<<(unsigned)rows, AT_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -156,3 +156,46 @@ def test_work_counts_match_page_sizes():
     assert need == 25169920
     assert R.prefill_flops(64, 128, need) == 412383969280
     assert R.decode_bytes(32, 1, 32768, 64, 128, 2048) == 269230080
+
+
+def _attn_prob(**kw):
+    p = Bd.CsaAttnProblem()
+    p.struct_size = ctypes.sizeof(Bd.CsaAttnProblem)
+    p.B, p.S_q, p.T, p.H, p.Dk, p.Dv = 32, 1, 32768, 64, 128, 128
+    p.q, p.k, p.v = 0x1000, 0x2000, 0x3000      # never dereferenced on the error paths
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_attention_struct_layout():
+    # uint32 + 6*int32 = 28 bytes, pointers from 32: 56 bytes
+    assert ctypes.sizeof(Bd.CsaAttnProblem) == 56
+    assert Bd.CsaAttnProblem.q.offset == 32
+
+
+def test_attention_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    # 32 rows, 16 chunks of 128 entries -> 8 workgroups per row
+    assert lib.csa_attention_workspace_size(ctypes.byref(_attn_prob()), 2048, ctypes.byref(n)) == 0
+    assert n.value == 32 * 8 * 64 * 128 * 4 + 2 * (32 * 8 * 64 * 4)
+    # many rows: one workgroup per row
+    assert lib.csa_attention_workspace_size(ctypes.byref(_attn_prob(B=4, S_q=512)), 2048, ctypes.byref(n)) == 0
+    assert n.value == 2048 * 64 * 128 * 4 + 2 * (2048 * 64 * 4)
+
+
+def test_attention_argument_errors(lib):
+    def call(p, idx=0x5000, n_sel=2048, scale=0.1, out=0x6000, ws=0x7000, ws_bytes=1 << 40):
+        return lib.csa_sparse_attention(ctypes.byref(p) if p is not None else None, idx, n_sel, scale, out, ws,
+                                        ws_bytes, None)
+    assert call(None) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(struct_size=8)) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(H=32)) == Bd.CSA_ERR_UNSUPPORTED
+    assert call(_attn_prob(Dv=64)) == Bd.CSA_ERR_UNSUPPORTED
+    assert call(_attn_prob(T=0)) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(), n_sel=0) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(), idx=None) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(), out=None) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(), scale=float("nan")) == Bd.CSA_ERR_INVALID
+    assert call(_attn_prob(), ws_bytes=16) == Bd.CSA_ERR_WORKSPACE
+    assert call(_attn_prob(), ws=0x7004) == Bd.CSA_ERR_INVALID
