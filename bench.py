@@ -13,6 +13,8 @@ Also reported on the same JSON line:
                 after the timed region);
   decode        the decode scan (B=32 x T=32768, k=2048) in GB/s against HBM
                 peak, K rotated over 4 copies so the 256 MB MALL cannot hold it;
+  attention     sparse attention over 2048 selected of T=32768 entries for the
+                same 32 rows (64 heads, d=128) in GB/s against HBM peak;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50]
@@ -154,6 +156,49 @@ def bench_decode(args, torch, L, csa_inputs, R):
                 workload="decode B=32 x 1 query, context 131072 (T=32768), H_I=64, d_I=128, k=2048, bf16")
 
 
+def bench_attention(args, torch, L, csa_inputs, R):
+    """Sparse attention over the decode workload's shape: 32 query rows, 64
+    heads, 2048 selected entries per row out of T=32768 compressed key and
+    value rows (bf16, d=128); K and V rotate over 4 copies (2 GiB in all) so
+    the 256 MB MALL cannot hold them."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    B, T, n_sel = 32, 32768, 2048
+    p = csa_inputs.make_attention(B, 1, T, n_sel=n_sel, seed=1006)
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k0, v0 = bf(p["q"]), bf(p["k"]), bf(p["v"])
+    idx = torch.from_numpy(p["idx"]).to(dev)
+    kv = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(3)]
+    lib = L.load_library()
+    probs = [L.make_attn_problem(q, kk, vv) for kk, vv in kv]
+    nws = L.attention_workspace_size(probs[0], n_sel)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 1, 64, 128), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    refs = [ctypes.byref(pp) for pp in probs]
+    ip, op, wp = ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr())
+
+    def call(i):
+        s = lib.csa_sparse_attention(refs[i % 4], ip, n_sel, p["scale"], op, wp, nws, stream)
+        if s != 0:
+            raise RuntimeError(lib.csa_last_error().decode())
+
+    nbytes = R.attention_bytes(B, B * n_sel, 64, 128, 128, n_sel)
+    steps = max(args.steps * 4, 40)
+    total_ms, avg_ms, med_ms, min_ms = _time_calls(torch, call, steps, args.warmup)
+    ms = total_ms / steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    _log(f"attention: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s")
+    del q, k0, v0, kv, idx, out, ws
+    torch.cuda.empty_cache()
+    return dict(value=round(gbps, 1), unit="GB/s", ms_per_call=round(ms, 5),
+                frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_call=nbytes, calls=steps,
+                kernels_per_call=2, kv_copies_rotated=4,
+                workload="sparse attention B=32 x 1 query, 64 heads, d=128, 2048 of T=32768 entries, bf16")
+
+
 def cpu_baseline(seconds, R):
     """Time the fp64 CPU oracle on the prefill workload: all rows when they fit
     the time budget (they do on a 16-core host: ~3 s), else a seeded sample of
@@ -200,6 +245,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only-decode", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (reference for the HBM byte counters)")
@@ -236,6 +282,7 @@ def main():
         return
     pf = bench_prefill(args, torch, L, csa_inputs, R)
     dec = None if args.no_decode else bench_decode(args, torch, L, csa_inputs, R)
+    att = None if args.no_attention else bench_attention(args, torch, L, csa_inputs, R)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, R)
 
     p = pf["p"]
@@ -277,6 +324,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "decode": dec,
+        "attention": att,
         "peak_mem_bytes": pf["peak_mem"],
         "workspace_bytes": pf["ws"],
         "materialised_score_tensor_bytes": R.materialised_score_bytes(1, p["S_q"], p["H"], p["T"]),

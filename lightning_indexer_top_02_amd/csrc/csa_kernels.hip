@@ -964,9 +964,10 @@ __device__ __forceinline__ uint32_t at_swz(int r, int col) {   // bf16 element (
   return (uint32_t)(r * AT_CHUNK * 2 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) << 1)));
 }
 
-__global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char ps[AT_H * AT_CHUNK * 2];      // P (bf16), head-major
   __shared__ __attribute__((aligned(16))) char vt[AT_D * AT_CHUNK * 2];      // V^T (bf16), dv-major
+  __shared__ bf16x8 qs[2][8][WAVE];                                          // Q in MFMA A-operand order
   __shared__ float red[4][AT_H];
   __shared__ float mrun[AT_H], lrun[AT_H], mnew_s[AT_H], alpha_s[AT_H];
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
@@ -977,12 +978,19 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
   const int32_t* irow = a.idx + (size_t)row * a.n_sel;
   const size_t kseq = (size_t)b * a.T;
 
-  bf16x8 A[2][8];
+  // index entries of this lane's key column and of this thread's two value
+  // rows (2p, 2p+1 with p = tid / 4; columns 32 * (tid % 4) .. + 31), for the
+  // first chunk here and for the next one at the end of each step
+  auto entry = [&](int j) { return j < a.n_sel ? irow[j] : -1; };
+  int ik = entry(split * AT_CHUNK + 32 * wv + (l & 31));
+  int iv0 = entry(split * AT_CHUNK + 2 * (tid >> 2)), iv1 = entry(split * AT_CHUNK + 2 * (tid >> 2) + 1);
+  // the query operand goes to LDS (wave w copies slices 2w, 2w+1), which
+  // leaves registers for the key and value rows of a chunk in flight together
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)row * AT_H + rt * 32 + (l & 31)) * AT_D);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) A[rt][kk] = src[2 * kk + (l >> 5)];
+    for (int h = 0; h < 2; ++h) qs[rt][2 * wv + h][l] = src[2 * (2 * wv + h) + (l >> 5)];
   }
   if (tid < AT_H) {
     mrun[tid] = -__builtin_inff();
@@ -993,30 +1001,27 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
   auto hrow = [&](int e) { return 8 * (e >> 2) + 4 * (l >> 5) + (e & 3); };
 
   for (int c = split; c < nchunk; c += a.nsplit) {
-    const int j0 = c * AT_CHUNK;
-    // this lane's key column for the logits, and this thread's value row
-    const int jk = j0 + 32 * wv + (l & 31);
-    const int ik = jk < a.n_sel ? irow[jk] : -1;
     const bool vk = ik >= 0 && ik < a.T;
-    const int jv = j0 + (tid >> 1);
-    const int iv = jv < a.n_sel ? irow[jv] : -1;
-    const bool vv = iv >= 0 && iv < a.T;
-    bf16x8 bk[8], vr[8];
-    {
+    const bool vv0 = iv0 >= 0 && iv0 < a.T, vv1 = iv1 >= 0 && iv1 < a.T;
+    bf16x8 bk[8], vr[2][4];
+    {                                                   // the chunk's key and value rows, all in flight
       const bf16x8* src = (const bf16x8*)(K + (kseq + (vk ? ik : 0)) * AT_D);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) bk[kk] = src[2 * kk + (l >> 5)];
+      const bf16x8* v0 = (const bf16x8*)(V + (kseq + (vv0 ? iv0 : 0)) * AT_D + (tid & 3) * 32);
+      const bf16x8* v1 = (const bf16x8*)(V + (kseq + (vv1 ? iv1 : 0)) * AT_D + (tid & 3) * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vr[0][i] = v0[i];
+        vr[1][i] = v1[i];
+      }
     }
+    __syncthreads();                                    // the query slices are in LDS (first chunk)
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[rt][kk], bk[kk], acc[rt], 0, 0, 0);
-    {                                                   // value rows load while the softmax statistics settle
-      const bf16x8* vsrc = (const bf16x8*)(V + (kseq + (vv ? iv : 0)) * AT_D + (tid & 1) * 64);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vr[i] = vsrc[i];
-    }
+      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qs[rt][kk][l], bk[kk], acc[rt], 0, 0, 0);
     // scaled logits; skipped entries at -inf; per-head max over the wave's 32 entries
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -1051,13 +1056,21 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
         for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, WAVE);
         if ((l & 31) == 0) red[wv][h] = x;
       }
-    // value row jv - j0 = tid / 2, columns (tid & 1) * 64 .. + 63, transposed
+    // value rows 2p, 2p+1 (columns 32 * (tid % 4) .. + 31), transposed: one
+    // 4-byte store per column holds both rows.  The pairs are formed on the
+    // 32-bit words (column 2u in the low half of word u, 2u+1 in the high half).
     {
-      const int kcol = tid >> 1;
+      const int kcol = 2 * (tid >> 2);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 w0 = __builtin_bit_cast(u32x4, vr[0][i]), w1 = __builtin_bit_cast(u32x4, vr[1][i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *(__bf16*)(vt + at_swz((tid & 1) * 64 + 8 * i + e, kcol)) = vr[i][e];
+        for (int u = 0; u < 4; ++u) {
+          const int col = (tid & 3) * 32 + 8 * i + 2 * u;
+          *(uint32_t*)(vt + at_swz(col, kcol)) = (w0[u] & 0xFFFFu) | (w1[u] << 16);
+          *(uint32_t*)(vt + at_swz(col + 1, kcol)) = (w0[u] >> 16) | (w1[u] & 0xFFFF0000u);
+        }
+      }
     }
     __syncthreads();
     if (tid < AT_H) {
@@ -1079,6 +1092,10 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
         o[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bv, o[rt], 0, 0, 0);
       }
     }
+    const int cn = c + a.nsplit;                        // the next chunk's entries
+    ik = entry(cn * AT_CHUNK + 32 * wv + (l & 31));
+    iv0 = entry(cn * AT_CHUNK + 2 * (tid >> 2));
+    iv1 = entry(cn * AT_CHUNK + 2 * (tid >> 2) + 1);
     __syncthreads();                                    // P, V^T and the stats are reused by the next chunk
   }
   const size_t pr = (size_t)row * a.nsplit + split;
@@ -1093,26 +1110,26 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
   }
 }
 
-// One workgroup per query row: o = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s
-// over the row's partial results (0 where no entry was valid).
-__global__ __launch_bounds__(AT_THREADS) void attn_combine_kernel(AttnArgs a) {
-  const int row = blockIdx.x;
+// One workgroup per (head, query row), one thread per output column:
+// o = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s over the row's partial
+// results (0 where no entry was valid).
+__global__ __launch_bounds__(AT_D) void attn_combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x, row = blockIdx.y, x = threadIdx.x;
   const size_t pr0 = (size_t)row * a.nsplit;
-  for (int x = threadIdx.x; x < AT_H * AT_D; x += AT_THREADS) {
-    const int h = x / AT_D;
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.mpart[(pr0 + s) * AT_H + h]);
-    float num = 0.f, den = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int s = 0; s < a.nsplit; ++s) {
-        const float ms = a.mpart[(pr0 + s) * AT_H + h];
-        const float f = ms == -__builtin_inff() ? 0.f : __expf(ms - M);
-        num += f * a.opart[(pr0 + s) * AT_H * AT_D + x];
-        den += f * a.lpart[(pr0 + s) * AT_H + h];
-      }
+  float M = -__builtin_inff();
+#pragma unroll 8
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.mpart[(pr0 + s) * AT_H + h]);
+  float num = 0.f, den = 0.f;
+  if (M != -__builtin_inff()) {
+#pragma unroll 8
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = a.mpart[(pr0 + s) * AT_H + h];
+      const float f = ms == -__builtin_inff() ? 0.f : __expf(ms - M);
+      num += f * a.opart[((pr0 + s) * AT_H + h) * AT_D + x];
+      den += f * a.lpart[(pr0 + s) * AT_H + h];
     }
-    a.out[(size_t)row * AT_H * AT_D + x] = den > 0.f ? num / den : 0.f;
   }
+  a.out[((size_t)row * AT_H + h) * AT_D + x] = den > 0.f ? num / den : 0.f;
 }
 
 // ============================================================ row sort
@@ -1287,7 +1304,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   attn_chunk_kernel<<<dim3(a.nsplit, (unsigned)rows), AT_THREADS, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_combine_kernel<<<(unsigned)rows, AT_THREADS, 0, st>>>(a);
+  attn_combine_kernel<<<dim3(AT_H, (unsigned)rows), AT_D, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -4,7 +4,9 @@ Counts only what the method must do:
 * prefill: 2*H*D flops per (query, visible key) pair, over rows that have more
   visible keys than k (a row with vis <= k selects every visible key and needs
   no score); the all-visible count is reported beside it;
-* decode: bytes of K, Q, w and the output indices, each moved once.
+* decode: bytes of K, Q, w and the output indices, each moved once;
+* sparse attention: bytes of the selected key and value rows, Q, the index
+  rows and the output, each moved once.
 """
 from __future__ import annotations
 
@@ -40,6 +42,12 @@ def prefill_flops(H: int, D: int, pairs: int) -> int:
 
 def decode_bytes(B: int, S_q: int, T: int, H: int, D: int, topk: int, elem: int = 2) -> int:
     return B * T * D * elem + B * S_q * H * D * elem + B * S_q * H * 4 + B * S_q * topk * 4
+
+
+def attention_bytes(rows: int, n_valid: int, H: int, Dk: int, Dv: int, n_sel: int, elem: int = 2) -> int:
+    """Sparse attention: the selected key and value rows (n_valid entries over
+    all rows), the queries, the index rows and the fp32 output, each moved once."""
+    return n_valid * (Dk + Dv) * elem + rows * H * Dk * elem + rows * n_sel * 4 + rows * H * Dv * 4
 
 
 def materialised_score_bytes(B: int, S: int, H: int, T: int) -> int:
