@@ -985,12 +985,14 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
   int ik = entry(split * AT_CHUNK + 32 * wv + (l & 31));
   int iv0 = entry(split * AT_CHUNK + 2 * (tid >> 2)), iv1 = entry(split * AT_CHUNK + 2 * (tid >> 2) + 1);
   // the query operand goes to LDS (wave w copies slices 2w, 2w+1), which
-  // leaves registers for the key and value rows of a chunk in flight together
+  // leaves registers for the key and value rows of a chunk in flight together;
+  // it is stored there once the first chunk's rows have been requested
+  bf16x8 qv[2][2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)row * AT_H + rt * 32 + (l & 31)) * AT_D);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) qs[rt][2 * wv + h][l] = src[2 * (2 * wv + h) + (l >> 5)];
+    for (int h = 0; h < 2; ++h) qv[rt][h] = src[2 * (2 * wv + h) + (l >> 5)];
   }
   if (tid < AT_H) {
     mrun[tid] = -__builtin_inff();
@@ -1016,23 +1018,38 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
         vr[1][i] = v1[i];
       }
     }
+    if (c == split) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) qs[rt][2 * wv + h][l] = qv[rt][h];
+    }
     __syncthreads();                                    // the query slices are in LDS (first chunk)
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qs[rt][kk][l], bk[kk], acc[rt], 0, 0, 0);
-    // scaled logits; skipped entries at -inf; per-head max over the wave's 32 entries
+    // scaled logits; skipped entries at -inf; per-head max over the wave's 32
+    // entries (the 32 butterflies run side by side, one exchange step at a
+    // time, so that their lane exchanges overlap instead of waiting in turn)
+    float red_v[16];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float x = vk ? a.scale * acc[rt][e] : -__builtin_inff();
-        acc[rt][e] = x;                                 // the logit, in place
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, WAVE));
-        if ((l & 31) == 0) red[wv][rt * 32 + hrow(e)] = x;
+        acc[rt][e] = vk ? a.scale * acc[rt][e] : -__builtin_inff();   // the logit, in place
+        red_v[e] = acc[rt][e];
       }
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], __shfl_xor(red_v[e], off, WAVE));
+      if ((l & 31) == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[wv][rt * 32 + hrow(e)] = red_v[e];
+      }
+    }
     __syncthreads();
     if (tid < AT_H) {
       const float cm = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
@@ -1042,8 +1059,9 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
     }
     __syncthreads();
     // p = exp(z - m_new) to LDS (bf16, A layout); per-head sums of the wave's p
+    // (of the rounded values the P.V product uses), butterflies side by side
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int h = rt * 32 + hrow(e);
@@ -1051,11 +1069,17 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
         const float pv = mn == -__builtin_inff() ? 0.f : __expf(acc[rt][e] - mn);
         const __bf16 pb = (__bf16)pv;
         *(__bf16*)(ps + at_swz(h, 32 * wv + (l & 31))) = pb;
-        float x = (float)pb;                            // the sum of what the P.V product uses
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) x += __shfl_xor(x, off, WAVE);
-        if ((l & 31) == 0) red[wv][h] = x;
+        red_v[e] = (float)pb;
       }
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red_v[e] += __shfl_xor(red_v[e], off, WAVE);
+      if ((l & 31) == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[wv][rt * 32 + hrow(e)] = red_v[e];
+      }
+    }
     // value rows 2p, 2p+1 (columns 32 * (tid % 4) .. + 31), transposed: one
     // 4-byte store per column holds both rows.  The pairs are formed on the
     // 32-bit words (column 2u in the low half of word u, 2u+1 in the high half).
