@@ -960,6 +960,16 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
 // operand reads of 32 rows at the same piece spread over the banks.
 // attn_combine_kernel merges the nsplit partial results of a row.
 
+// Lane exchanges inside 16-lane rows through DPP (no LDS round trip):
+// quad_perm [1,0,3,2] and [2,3,0,1], then the mirrored half row and row, pair
+// every lane with one whose partial covers the other lanes of its 2, 4, 8 and
+// 16 group; the last step (lane ^ 16) goes through ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
 __device__ __forceinline__ uint32_t at_swz(int r, int col) {   // bf16 element (r, col) of a 128-wide tile
   return (uint32_t)(r * AT_CHUNK * 2 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) << 1)));
 }
@@ -1042,9 +1052,15 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
         red_v[e] = acc[rt][e];
       }
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1)
+      for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], dpp_f32<DPP_XOR1>(red_v[e]));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], __shfl_xor(red_v[e], off, WAVE));
+      for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], dpp_f32<DPP_XOR2>(red_v[e]));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], dpp_f32<DPP_HALF_MIRROR>(red_v[e]));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], dpp_f32<DPP_MIRROR>(red_v[e]));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], __shfl_xor(red_v[e], 16, WAVE));
       if ((l & 31) == 0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) red[wv][rt * 32 + hrow(e)] = red_v[e];
@@ -1072,9 +1088,15 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
         red_v[e] = (float)pb;
       }
 #pragma unroll
-      for (int off = 1; off < 32; off <<= 1)
+      for (int e = 0; e < 16; ++e) red_v[e] += dpp_f32<DPP_XOR1>(red_v[e]);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) red_v[e] += __shfl_xor(red_v[e], off, WAVE);
+      for (int e = 0; e < 16; ++e) red_v[e] += dpp_f32<DPP_XOR2>(red_v[e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red_v[e] += dpp_f32<DPP_HALF_MIRROR>(red_v[e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red_v[e] += dpp_f32<DPP_MIRROR>(red_v[e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red_v[e] += __shfl_xor(red_v[e], 16, WAVE);
       if ((l & 31) == 0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) red[wv][rt * 32 + hrow(e)] = red_v[e];
