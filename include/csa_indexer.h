@@ -188,6 +188,22 @@ csa_status csa_attention_workspace_size(const csa_attn_problem* prob, int32_t n_
 csa_status csa_sparse_attention(const csa_attn_problem* prob, const int32_t* idx, int32_t n_sel, float scale,
                                 float* out, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Union of several selections per row (multi-layer selection: the
+ * FlashMemory-DeepSeek-V4 review, "What carries the argument", places its
+ * Memory Indexer on three layers and combines their keep decisions with a
+ * logical OR while decoding).  For each of `rows` rows: the set of distinct
+ * values v with 0 <= v < T found in row r of any of the L lists (list i is a
+ * device array [rows, widths[i]] int32; other entries are ignored), written
+ * to out_idx [rows, cap] in ascending order, then -1; out_count [rows]
+ * (optional, may be NULL) receives the true size of the union, which may
+ * exceed cap (then the cap smallest indices are written).  lists and widths
+ * are HOST arrays of L entries; 1 <= L <= CSA_MAX_UNION_LISTS; 1 <= T <=
+ * CSA_MAX_UNION_T (CSA_ERR_UNSUPPORTED above); cap >= 1.  No workspace. */
+#define CSA_MAX_UNION_LISTS 8
+#define CSA_MAX_UNION_T (1 << 20)
+csa_status csa_union_rows(const int32_t* const* lists, const int32_t* widths, int32_t L, int64_t rows,
+                          int32_t T, int32_t cap, int32_t* out_idx, int32_t* out_count, void* hip_stream);
+
 const char* csa_status_str(csa_status s); /* static string, never NULL */
 const char* csa_last_error(void);         /* thread-local detail of this thread's last error */
 int csa_version(void);                    /* major*10000 + minor*100 + patch */

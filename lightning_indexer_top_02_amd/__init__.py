@@ -10,5 +10,6 @@ from ._binding import (  # noqa: F401
     OP_DECODE, OP_INTERLEAVED, OP_PREFILL, OP_RECALL, OP_THRESHOLD, CsaError, CsaProblem,
     index_threshold_select, index_topk_decode, index_topk_interleaved, index_topk_prefill,
     load_library, make_problem, set_recall, version, workspace_size,
-    CsaAttnProblem, attention_workspace_size, make_attn_problem, sparse_attention,
+    CsaAttnProblem, attention_workspace_size, make_attn_problem, sparse_attention, union_rows,
+    MultiLayerSelector,
 )

@@ -64,6 +64,8 @@ _SIGS = {
     "csa_set_recall": (_i32, [_vp, _i32, _vp, _i32, ctypes.c_int64, _i32, _vp, _vp, _sz, _vp]),
     "csa_attention_workspace_size": (_i32, [_PA, _i32, ctypes.POINTER(_sz)]),
     "csa_sparse_attention": (_i32, [_PA, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
+    "csa_union_rows": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, ctypes.c_int64, _i32, _i32, _vp,
+                              _vp, _vp]),
     "csa_status_str": (ctypes.c_char_p, [_i32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_version": (ctypes.c_int, []),
@@ -295,3 +297,80 @@ def sparse_attention(q, k, v, idx, *, scale=None, out=None, workspace=None):
     _check(load_library().csa_sparse_attention(ctypes.byref(prob), _ptr(idx), int(n_sel), scale, _ptr(o),
                                                _ptr(ws), _nbytes(ws), _stream_handle()))
     return o
+
+
+def union_rows(lists, T, cap, *, with_count=True):
+    """Per-row union of index lists (each an int32 GPU tensor [..., width] with
+    the same leading shape): ascending distinct indices in [0, T), -1 padded
+    to `cap`; also the true union sizes (int32, leading shape) if with_count."""
+    torch = _torch()
+    if not lists:
+        raise ValueError("need at least one list")
+    lead = lists[0].shape[:-1]
+    for t in lists:
+        if t.dtype != torch.int32 or not (t.is_cuda and t.is_contiguous()):
+            raise TypeError("lists must be contiguous int32 GPU tensors")
+        if t.shape[:-1] != lead:
+            raise ValueError("lists must share their leading shape")
+    rows = 1
+    for d in lead:
+        rows *= int(d)
+    ptrs = (_vp * len(lists))(*[_ptr(t) for t in lists])
+    widths = (_i32 * len(lists))(*[int(t.shape[-1]) for t in lists])
+    out = torch.empty(tuple(lead) + (int(cap),), dtype=torch.int32, device=lists[0].device)
+    cnt = torch.empty(tuple(lead), dtype=torch.int32, device=lists[0].device) if with_count else None
+    _check(load_library().csa_union_rows(ptrs, widths, len(lists), rows, int(T), int(cap), _ptr(out),
+                                         _ptr(cnt) if cnt is not None else None, _stream_handle()))
+    return (out, cnt) if with_count else out
+
+
+class MultiLayerSelector:
+    """OR-union of several indexer layers' threshold selections, recomputed
+    every `tau` decode steps and reused in between (FlashMemory-DeepSeek-V4
+    review: Memory Indexer on three layers, keep decisions OR-ed, a decode
+    trigger interval of 64 steps).  Each layer's selection may run on its own
+    HIP stream (`overlap=True`), joined before the union on the caller's
+    current stream.  All compute is in the library's kernels."""
+
+    def __init__(self, tau=64, prob_threshold=0.5, logit_bias=0.0, cap=2048, union_cap=None, overlap=False):
+        self.tau = int(tau)
+        self.prob_threshold = float(prob_threshold)
+        self.logit_bias = float(logit_bias)
+        self.cap = int(cap)
+        self.union_cap = int(union_cap) if union_cap is not None else None
+        self.overlap = bool(overlap)
+        self.refreshes = 0
+        self._cached = None
+
+    def select(self, step, layers, *, m=4, q_pos0=0, kv_len=None, causal=True):
+        """layers: sequence of (q, k, w) indexer inputs, one per layer, sharing
+        B, S_q and T.  Returns (union [B, S_q, union_cap], count [B, S_q])."""
+        if self._cached is not None and step % self.tau != 0:
+            return self._cached
+        torch = _torch()
+        T = layers[0][1].shape[1]
+        ucap = self.union_cap if self.union_cap is not None else min(T, self.cap * len(layers))
+        main = torch.cuda.current_stream()
+        sels = []
+        if self.overlap:
+            streams = [torch.cuda.Stream() for _ in layers]
+            for s in streams:
+                s.wait_stream(main)
+            for (q, k, w), s in zip(layers, streams):
+                with torch.cuda.stream(s):
+                    idx, _ = index_threshold_select(q, k, w, self.cap, prob_threshold=self.prob_threshold,
+                                                    logit_bias=self.logit_bias, m=m, q_pos0=q_pos0,
+                                                    kv_len=kv_len, causal=causal)
+                    sels.append(idx)
+            for s, idx in zip(streams, sels):
+                main.wait_stream(s)
+                idx.record_stream(main)
+        else:
+            for q, k, w in layers:
+                idx, _ = index_threshold_select(q, k, w, self.cap, prob_threshold=self.prob_threshold,
+                                                logit_bias=self.logit_bias, m=m, q_pos0=q_pos0, kv_len=kv_len,
+                                                causal=causal)
+                sels.append(idx)
+        self._cached = union_rows(sels, T, ucap)
+        self.refreshes += 1
+        return self._cached

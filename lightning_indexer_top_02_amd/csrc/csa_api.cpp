@@ -421,6 +421,33 @@ csa_status csa_sparse_attention(const csa_attn_problem* prob, const int32_t* idx
   }
 }
 
+csa_status csa_union_rows(const int32_t* const* lists, const int32_t* widths, int32_t L, int64_t rows, int32_t T,
+                          int32_t cap, int32_t* out_idx, int32_t* out_count, void* hip_stream) {
+  try {
+    static_assert(CSA_MAX_UNION_LISTS == csa::UN_MAX_LISTS && CSA_MAX_UNION_T == csa::UN_MAX_T, "union limits");
+    if (L < 1 || L > CSA_MAX_UNION_LISTS) return fail(CSA_ERR_INVALID, "L=%d outside [1, %d]", L, CSA_MAX_UNION_LISTS);
+    if (!lists || !widths) return fail(CSA_ERR_INVALID, "lists and widths must not be NULL");
+    if (rows < 0) return fail(CSA_ERR_INVALID, "rows=%lld < 0", (long long)rows);
+    if (T < 1 || cap < 1) return fail(CSA_ERR_INVALID, "T and cap must be >= 1");
+    if (T > CSA_MAX_UNION_T) return fail(CSA_ERR_UNSUPPORTED, "T=%d > %d", T, CSA_MAX_UNION_T);
+    if (rows > (1ll << 31) - 1) return fail(CSA_ERR_UNSUPPORTED, "too many rows");
+    csa::UnionArgs a{};
+    for (int i = 0; i < L; ++i) {
+      if (widths[i] < 1) return fail(CSA_ERR_INVALID, "widths[%d]=%d < 1", i, widths[i]);
+      if (rows > 0 && !lists[i]) return fail(CSA_ERR_INVALID, "lists[%d] is NULL", i);
+      a.list[i] = lists[i];
+      a.width[i] = widths[i];
+    }
+    if (rows > 0 && !out_idx) return fail(CSA_ERR_INVALID, "out_idx must not be NULL");
+    a.L = L; a.T = T; a.cap = cap; a.out_idx = out_idx; a.out_count = out_count;
+    hipError_t e = csa::launch_union(a, rows, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "union launch failed: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
 csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref, int32_t n_ref, int64_t rows,
                           int32_t T, float* out_recall, void* ws, size_t ws_bytes, void* hip_stream) {
   (void)ws;

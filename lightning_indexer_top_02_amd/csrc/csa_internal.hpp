@@ -84,6 +84,23 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
+// Per-row union of several index lists (multi-layer selection).
+constexpr int UN_MAX_LISTS = 8;
+constexpr int UN_MAX_T = 1 << 20;      // keys covered by the LDS bitmap (128 KiB)
+constexpr int UN_THREADS = 1024;
+
+struct UnionArgs {
+  const int32_t* list[UN_MAX_LISTS];   // list i: [rows][width[i]]
+  int width[UN_MAX_LISTS];
+  int L;
+  int T;
+  int cap;
+  int32_t* out_idx;                    // [rows][cap]
+  int32_t* out_count;                  // [rows]
+};
+
+hipError_t launch_union(const UnionArgs& a, long long rows, hipStream_t st);
+
 // mfma: the bf16 H=64 D=128 MFMA kernel; otherwise the generic kernel for a.bf16.
 hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, hipStream_t st);
 // Resident workgroups per CU of the chosen prefill kernel (>= 1).

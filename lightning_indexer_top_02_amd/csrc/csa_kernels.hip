@@ -1178,6 +1178,58 @@ __global__ __launch_bounds__(AT_D) void attn_combine_kernel(AttnArgs a) {
   a.out[((size_t)row * AT_H + h) * AT_D + x] = den > 0.f ? num / den : 0.f;
 }
 
+// ============================================================ union of selections
+//
+// Multi-layer selection (FlashMemory's Memory Indexer on three layers whose
+// decisions are OR-ed while decoding): per row, the union of L index lists.
+// One workgroup per row marks every valid entry (0 <= v < T) in an LDS bitmap
+// of T bits, then thread t takes a contiguous run of bitmap words, counts its
+// bits, and after a block-wide prefix sum writes its indices in ascending
+// order: the union sorted by index, deterministic.
+
+__global__ __launch_bounds__(UN_THREADS) void union_rows_kernel(UnionArgs a) {
+  __shared__ uint32_t words[UN_MAX_T / 32];
+  __shared__ int wsum[UN_THREADS / WAVE];
+  constexpr int NW = UN_THREADS / WAVE;
+  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  const long long row = blockIdx.x;
+  const int nwords = (a.T + 31) / 32;
+  for (int i = tid; i < nwords; i += UN_THREADS) words[i] = 0u;
+  __syncthreads();
+  for (int li = 0; li < a.L; ++li) {
+    const int n = a.width[li];
+    const int32_t* src = a.list[li] + row * n;
+    for (int e = tid; e < n; e += UN_THREADS) {
+      const int v = src[e];
+      if (v >= 0 && v < a.T) atomicOr(&words[v >> 5], 1u << (v & 31));
+    }
+  }
+  __syncthreads();
+  const int per = (nwords + UN_THREADS - 1) / UN_THREADS;
+  const int w0 = tid * per, w1 = min(w0 + per, nwords);
+  int mine = 0;
+  for (int i = w0; i < w1; ++i) mine += __popc(words[i]);
+  const int incl = wave_incl_scan(mine);
+  if (l == WAVE - 1) wsum[wv] = incl;
+  __syncthreads();
+  int off = incl - mine, total = 0;
+  for (int j = 0; j < NW; ++j) {
+    off += j < wv ? wsum[j] : 0;
+    total += wsum[j];
+  }
+  int32_t* out = a.out_idx + row * a.cap;
+  for (int i = w0; i < w1 && off < a.cap; ++i) {
+    uint32_t m = words[i];
+    while (m && off < a.cap) {
+      const int bit = __ffs(m) - 1;
+      out[off++] = i * 32 + bit;
+      m &= m - 1;
+    }
+  }
+  for (int e = min(total, a.cap) + tid; e < a.cap; e += UN_THREADS) out[e] = -1;
+  if (tid == 0 && a.out_count) a.out_count[row] = total;
+}
+
 // ============================================================ row sort
 //
 // Sorts each row of `len` (index, score) pairs by (score desc, index asc);
@@ -1351,6 +1403,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   attn_combine_kernel<<<dim3(AT_H, (unsigned)rows), AT_D, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const UnionArgs& a, long long rows, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  union_rows_kernel<<<(unsigned)rows, UN_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -10,3 +10,4 @@ from .csa_oracle import (  # noqa: F401
     row_score_vector, RowScorer,
 )
 from .csa_attention_oracle import attention_row, oracle_attention  # noqa: F401
+from .csa_union_oracle import oracle_union, oracle_multilayer  # noqa: F401

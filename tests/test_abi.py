@@ -199,3 +199,20 @@ def test_attention_argument_errors(lib):
     assert call(_attn_prob(), scale=float("nan")) == Bd.CSA_ERR_INVALID
     assert call(_attn_prob(), ws_bytes=16) == Bd.CSA_ERR_WORKSPACE
     assert call(_attn_prob(), ws=0x7004) == Bd.CSA_ERR_INVALID
+
+
+def test_union_argument_errors(lib):
+    P = ctypes.c_void_p * 2
+    W = ctypes.c_int32 * 2
+
+    def call(L=2, rows=4, T=100, cap=8, lists=(0x1000, 0x2000), widths=(4, 4), out=0x3000):
+        return lib.csa_union_rows(P(*lists), W(*widths), L, rows, T, cap, out, None, None)
+    assert call(L=0) == Bd.CSA_ERR_INVALID
+    assert call(L=9) == Bd.CSA_ERR_INVALID
+    assert call(rows=-1) == Bd.CSA_ERR_INVALID
+    assert call(T=0) == Bd.CSA_ERR_INVALID
+    assert call(cap=0) == Bd.CSA_ERR_INVALID
+    assert call(T=(1 << 20) + 1) == Bd.CSA_ERR_UNSUPPORTED
+    assert call(widths=(4, 0)) == Bd.CSA_ERR_INVALID
+    assert call(lists=(0x1000, 0)) == Bd.CSA_ERR_INVALID
+    assert call(out=None) == Bd.CSA_ERR_INVALID

@@ -1,0 +1,68 @@
+"""GPU checks of csa_union_rows and the multi-layer selector (integer work:
+bit-exact against the CPU oracle)."""
+import numpy as np
+import pytest
+
+import csa_inputs
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import lightning_indexer_top_02_amd as L  # noqa: E402
+
+
+def _say(msg):
+    print(f"[csa-test] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("T,widths,cap", [(1000, (64, 200, 17), 300),      # union larger than some lists
+                                          (1000, (64, 200, 17), 40),       # cap below the union size
+                                          (1 << 20, (2048, 2048), 4096),   # the largest T the bitmap covers
+                                          (33, (5,), 8)])                  # one list, tiny T
+def test_union_matches_oracle(T, widths, cap):
+    rng = np.random.default_rng(T + cap)
+    rows = (3, 5)
+    lists = [rng.integers(-2, T + 3, size=rows + (w,)).astype(np.int32) for w in widths]
+    lists[0][0, 0, :3] = lists[-1][0, 0, :3]                               # shared entries
+    _say(f"union T={T} widths={widths} cap={cap}")
+    out, cnt = L.union_rows([torch.from_numpy(x).cuda() for x in lists], T, cap)
+    torch.cuda.synchronize()
+    ref, rcnt = oracle.oracle_union(lists, T, cap)
+    assert (out.cpu().numpy() == ref).all()
+    assert (cnt.cpu().numpy() == rcnt).all()
+
+
+def _layer(seed, S_q=3, T=500):
+    p = csa_inputs.make_integer(B=2, S_q=S_q, T=T, H=64, D=128, m=4, topk=64, q_pos0=4 * T - S_q, seed=seed,
+                                qk_range=2, w_range=2)
+    p["q"] = csa_inputs.f32_to_bf16_bits(p["q"])
+    p["k"] = csa_inputs.f32_to_bf16_bits(p["k"])
+    p["dtype"] = "bf16"
+    return p
+
+
+def _dev(p):
+    q = torch.from_numpy(p["q"].view(np.int16)).view(torch.bfloat16).cuda()
+    k = torch.from_numpy(p["k"].view(np.int16)).view(torch.bfloat16).cuda()
+    return q, k, torch.from_numpy(p["w"]).cuda()
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_multilayer_union_and_refresh(overlap):
+    probs = [_layer(s) for s in (21, 22, 23)]
+    layers = [_dev(p) for p in probs]
+    cap, ucap = 96, 320
+    sel = L.MultiLayerSelector(tau=4, prob_threshold=0.5, cap=cap, union_cap=ucap, overlap=overlap)
+    _say(f"multi-layer union, overlap={overlap}")
+    u, c = sel.select(0, layers, m=4, q_pos0=probs[0]["q_pos0"])
+    torch.cuda.synchronize()
+    ref, rcnt = oracle.oracle_multilayer(probs, 0.5, cap, ucap)
+    assert (u.cpu().numpy() == ref).all()
+    assert (c.cpu().numpy() == rcnt).all()
+    for step in (1, 2, 3):                                               # reused between refreshes
+        assert sel.select(step, layers, m=4, q_pos0=probs[0]["q_pos0"])[0] is u
+    assert sel.refreshes == 1
+    u2, _ = sel.select(4, layers, m=4, q_pos0=probs[0]["q_pos0"])
+    torch.cuda.synchronize()
+    assert sel.refreshes == 2 and (u2.cpu().numpy() == ref).all()
