@@ -226,7 +226,7 @@ csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap,
     }
     if (op == CSA_OP_DECODE && prob->S_q > CSA_MAX_DECODE_SQ)
       return fail(CSA_ERR_UNSUPPORTED, "decode needs S_q <= %d", CSA_MAX_DECODE_SQ);
-    if (op == CSA_OP_DECODE && decode_fast(prob)) {
+    if ((op == CSA_OP_DECODE || op == CSA_OP_THRESHOLD) && decode_fast(prob)) {
       *bytes = plan_decode(prob, k_or_cap, flags).total;
     } else {
       *bytes = plan_prefill(prob, k_or_cap, parts, k_or_cap * parts, flags).total;
@@ -236,6 +236,47 @@ csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap,
     return fail(CSA_ERR_INVALID, "internal error");
   }
 }
+
+}  // extern "C"
+
+namespace {
+
+// Decode-shaped problems (bf16, H=64, D=128, S_q <= CSA_MAX_DECODE_SQ): the
+// key scan, then the per-row select; thr != 0 selects threshold mode
+// (survivors = keys >= thr, counted into out_count, the best kk written).
+csa_status run_decode(const csa_problem* prob, int kk, uint32_t flags, unsigned long long thr, int32_t* out_idx,
+                      float* out_score, int32_t* out_count, void* ws, size_t ws_bytes, void* hip_stream) {
+  const DecodePlan d = plan_decode(prob, kk, flags);
+  if (ws_bytes < d.total || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, d.total);
+  if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
+  const bool sorted = (flags & CSA_SORTED) != 0;
+  float* score_dst = out_score;
+  if (sorted && !score_dst) score_dst = (float*)((char*)ws + d.score_bytes + d.bound_bytes);
+  csa::DecodeArgs a{};
+  a.q = prob->q; a.k = prob->k; a.w = prob->w; a.kv_len = prob->kv_len;
+  a.B = prob->B; a.S_q = prob->S_q; a.T = prob->T; a.m = prob->m; a.q_pos0 = prob->q_pos0;
+  a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
+  a.thr_fixed = thr;
+  a.out_count = out_count;
+  a.scores = (float*)ws;
+  a.bounds = (uint4*)((char*)ws + d.score_bytes);
+  a.nbw = d.nbw;
+  a.kk = kk;
+  a.out_idx = out_idx;
+  a.out_score = score_dst;
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e = csa::launch_decode(a, d.nsplit, st);
+  if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+  if (sorted) {
+    e = csa::launch_sort_rows(out_idx, score_dst, (long long)prob->B * prob->S_q, kk, st);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "sort launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
 
 csa_status csa_index_topk_prefill(const csa_problem* prob, int32_t topk, uint32_t flags, int32_t* out_idx,
                                   float* out_score, void* ws, size_t ws_bytes, void* hip_stream) {
@@ -265,30 +306,7 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
     if (!decode_fast(prob))
       return run_prefill_family(prob, csa::MODE_TOPK, topk, 1, flags, 0ull, out_idx, out_score, nullptr, ws,
                                 ws_bytes, hip_stream);
-    const DecodePlan d = plan_decode(prob, topk, flags);
-    if (ws_bytes < d.total || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, d.total);
-    if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
-    const bool sorted = (flags & CSA_SORTED) != 0;
-    float* score_dst = out_score;
-    if (sorted && !score_dst) score_dst = (float*)((char*)ws + d.score_bytes + d.bound_bytes);
-    csa::DecodeArgs a{};
-    a.q = prob->q; a.k = prob->k; a.w = prob->w; a.kv_len = prob->kv_len;
-    a.B = prob->B; a.S_q = prob->S_q; a.T = prob->T; a.m = prob->m; a.q_pos0 = prob->q_pos0;
-    a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
-    a.scores = (float*)ws;
-    a.bounds = (uint4*)((char*)ws + d.score_bytes);
-    a.nbw = d.nbw;
-    a.kk = topk;
-    a.out_idx = out_idx;
-    a.out_score = score_dst;
-    hipStream_t st = (hipStream_t)hip_stream;
-    hipError_t e = csa::launch_decode(a, d.nsplit, st);
-    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
-    if (sorted) {
-      e = csa::launch_sort_rows(out_idx, score_dst, (long long)prob->B * prob->S_q, topk, st);
-      if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "sort launch failed: %s", hipGetErrorString(e));
-    }
-    return ok();
+    return run_decode(prob, topk, flags, 0ull, out_idx, out_score, nullptr, ws, ws_bytes, hip_stream);
   } catch (...) {
     return fail(CSA_ERR_INVALID, "internal error");
   }
@@ -317,6 +335,8 @@ csa_status csa_index_threshold_select(const csa_problem* prob, float prob_thresh
     if (u == 0x80000000u) u = 0u;
     const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     const unsigned long long thr = (unsigned long long)ord << 32;
+    if (decode_fast(prob))                            // few query rows: the decode key scan and select
+      return run_decode(prob, cap, flags, thr, out_idx, out_score, out_count, ws, ws_bytes, hip_stream);
     return run_prefill_family(prob, csa::MODE_THRESHOLD, cap, 1, flags, thr, out_idx, out_score, out_count, ws,
                               ws_bytes, hip_stream);
   } catch (...) {

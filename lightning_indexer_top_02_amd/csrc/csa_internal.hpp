@@ -49,6 +49,8 @@ struct DecodeArgs {
   int B, S_q, T, m;
   long long q_pos0;
   int causal;
+  unsigned long long thr_fixed;  // threshold mode: smallest surviving key (0: top-k mode)
+  int32_t* out_count;   // threshold mode: survivors per row
   float* scores;        // [B*S_q][T + DEC_PAD] fp32 workspace
   uint4* bounds;        // [B*S_q][nbw] per-wave selection bounds {order bits, count, max order bits, 0}
   int nbw;              // bounds per row: DEC_THREADS / WAVE per key chunk

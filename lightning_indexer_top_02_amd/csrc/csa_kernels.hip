@@ -799,22 +799,46 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
       const int s = e0 + j * WAVE;
       v[j] = sc[s < vis ? s : last];
     }
-    if (vis <= a.kk) {                                // every visible key, in element order
+    // Threshold mode: the survivors are the keys >= thr_fixed, i.e. scoring
+    // >= sf (the smallest fp32 score above the threshold; the float compare
+    // agrees with the order bits, -0 included).  Their count is written out;
+    // when it exceeds kk (the cap) the survivors' best kk are the row's top kk
+    // and the top-k select below runs unchanged.
+    const bool thr = a.thr_fixed != 0ull;
+    const float sf = thr ? key_score(a.thr_fixed) : -__builtin_inff();
+    bool all = vis <= a.kk;
+    if (thr) {
       int mine = 0;
 #pragma unroll
-      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(e0 + j * WAVE < vis));
+      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(e0 + j * WAVE < vis && v[j] >= sf));
       if (l == 0) wcnt[wv] = mine;
       __syncthreads();
-      int off = 0;
-      for (int j = 0; j < wv; ++j) off += wcnt[j];
+      int tot = 0;
+      for (int j = 0; j < NW; ++j) tot += wcnt[j];
+      if (tid == 0) a.out_count[row] = tot;
+      all = tot <= a.kk;
+      __syncthreads();                                // wcnt is reused below
+    }
+    if (all) {                                        // every visible key (survivor), in element order
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(e0 + j * WAVE < vis && v[j] >= sf));
+      if (l == 0) wcnt[wv] = mine;
+      __syncthreads();
+      int off = 0, tot = 0;
+      for (int j = 0; j < NW; ++j) {
+        off += j < wv ? wcnt[j] : 0;
+        tot += wcnt[j];
+      }
 #pragma unroll
       for (int j = 0; j < DEC_REG; ++j) {
         const int s = e0 + j * WAVE;
-        const u64 m = ballot(s < vis);
-        if (s < vis) emit_key(make_key(v[j], (uint32_t)s), off + lanes_below(m), a.kk, oi, os);
+        const bool keep = s < vis && v[j] >= sf;
+        const u64 m = ballot(keep);
+        if (keep) emit_key(make_key(v[j], (uint32_t)s), off + lanes_below(m), a.kk, oi, os);
         off += __popcll(m);
       }
-      w = vis;
+      w = tot;
     } else {
       // [1] bounds -> L (order bits), their count, row max; clear the histogram meanwhile
       const uint32_t P0 = wave_min_u32(bd.y ? bd.x : ~0u);
@@ -915,7 +939,20 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
   }
   if (dense) {                                        // uniform: every decision above came from LDS
     __syncthreads();
-    const u64 T = block_select_kth_dense<DEC_SEL_THREADS>(sc, vis, a.kk, hist, red);
+    u64 T = 0ull;
+    if (a.thr_fixed != 0ull && vis > DEC_REG * DEC_SEL_THREADS) {   // threshold mode, long row: count first
+      int mine = 0;
+      for (int s = tid; s < vis; s += DEC_SEL_THREADS) mine += make_key(sc[s], (uint32_t)s) >= a.thr_fixed;
+      mine = wave_sum_i32(mine);
+      if (l == 0) wcnt[wv] = mine;
+      __syncthreads();
+      int tot = 0;
+      for (int j = 0; j < NW; ++j) tot += wcnt[j];
+      if (tid == 0) a.out_count[row] = tot;
+      __syncthreads();
+      if (tot <= a.kk) T = a.thr_fixed;
+    }
+    if (T == 0ull) T = block_select_kth_dense<DEC_SEL_THREADS>(sc, vis, a.kk, hist, red);
     for (int base = 0; base < vis; base += DEC_SEL_THREADS) {
       const int s = base + tid;
       const u64 x = s < vis ? make_key(sc[s], (uint32_t)s) : 0ull;

@@ -80,3 +80,35 @@ def test_threshold_nesting_gpu():
         if prev is not None:
             assert all(a <= b for a, b in zip(sets, prev))
         prev = sets
+
+
+def _decode_integer(B=3, S_q=2, T=3000, seed=31, kv_len=None):
+    """Few query rows against long key rows: the decode key scan path."""
+    p = csa_inputs.make_integer(B=B, S_q=S_q, T=T, H=64, D=128, m=4, topk=64, q_pos0=4 * T - S_q, seed=seed,
+                                qk_range=2, w_range=2)
+    p["q"] = csa_inputs.f32_to_bf16_bits(p["q"])
+    p["k"] = csa_inputs.f32_to_bf16_bits(p["k"])
+    p["dtype"] = "bf16"
+    if kv_len is not None:
+        p["kv_len"] = np.asarray(kv_len, dtype=np.int32)
+    return p
+
+
+@pytest.mark.parametrize("case,cap,tau,bias", [("over_cap", 200, 0.5, 0.0),       # survivors > cap
+                                               ("under_cap", 4096, 0.5, 0.0),     # every survivor fits
+                                               ("high_threshold", 300, 0.5, -6.0),
+                                               ("kv_len", 256, 0.5, 0.0),         # short and empty rows
+                                               ("long_rows", 1024, 0.5, 2.0)])    # rows past the register tile
+def test_threshold_decode_path_exact(case, cap, tau, bias):
+    if case == "kv_len":
+        p = _decode_integer(kv_len=[3000, 170, 0])
+    elif case == "long_rows":
+        p = _decode_integer(B=2, S_q=1, T=40000, seed=32)
+    else:
+        p = _decode_integer()
+    ref_i, ref_c, ref_s = oracle.oracle_threshold(p, tau, bias, cap)
+    idx, cnt, sc = _thr(p, cap, tau, bias)
+    assert (cnt == ref_c).all()
+    check_exact(idx, ref_i, sc, ref_s)
+    idx_s, cnt_s, sc_s = _thr(p, cap, tau, bias, sorted=True)
+    assert (idx_s == ref_i).all() and (cnt_s == ref_c).all()
