@@ -15,6 +15,8 @@ Also reported on the same JSON line:
                 peak, K rotated over 4 copies so the 256 MB MALL cannot hold it;
   attention     sparse attention over 2048 selected of T=32768 entries for the
                 same 32 rows (64 heads, d=128) in GB/s against HBM peak;
+  multilayer    one refresh of a three-layer threshold selection with OR-union
+                at the decode shape, in GB/s of indexer keys against HBM peak;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50]
@@ -199,6 +201,39 @@ def bench_attention(args, torch, L, csa_inputs, R):
                 workload="sparse attention B=32 x 1 query, 64 heads, d=128, 2048 of T=32768 entries, bf16")
 
 
+def bench_multilayer(args, torch, L, csa_inputs, R):
+    """FlashMemory-style multi-layer selection at the decode shape: three
+    indexer layers (each B=32, T=32768, H_I=64, d_I=128, its own keys), a
+    sigmoid-threshold selection (tau=0.5, cap 2048) per layer, OR-union of the
+    three.  One refresh (what runs every 64 decode steps) is timed."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    layers = []
+    for li in range(3):
+        p = csa_inputs.make_decode(seed=1007 + li, name=f"layer {li}")
+        layers.append((torch.from_numpy(p["q"].view(np.int16)).view(torch.bfloat16).to(dev),
+                       torch.from_numpy(p["k"].view(np.int16)).view(torch.bfloat16).to(dev),
+                       torch.from_numpy(p["w"]).to(dev)))
+    sel = L.MultiLayerSelector(tau=64, prob_threshold=0.5, cap=2048, union_cap=3 * 2048)
+
+    def call(i):
+        sel.select(64 * i, layers, m=p["m"], q_pos0=p["q_pos0"])     # every call is a refresh step
+
+    nbytes = 3 * R.decode_bytes(p["B"], 1, p["T"], p["H"], p["D"], 2048)
+    steps = max(args.steps, 40)
+    total_ms, avg_ms, med_ms, min_ms = _time_calls(torch, call, steps, min(args.warmup, 20))
+    ms = total_ms / steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    _log(f"multi-layer refresh: {ms * 1e3:.1f} us per refresh, {gbps:.0f} GB/s")
+    del layers, sel
+    torch.cuda.empty_cache()
+    return dict(value=round(gbps, 1), unit="GB/s", ms_per_refresh=round(ms, 5),
+                frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_refresh=nbytes, refreshes=steps,
+                refresh_interval_steps=64,
+                workload="3 indexer layers x decode B=32, T=32768, H_I=64, d_I=128; threshold tau=0.5, cap 2048; "
+                         "OR-union (cap 6144)")
+
+
 def cpu_baseline(seconds, R):
     """Time the fp64 CPU oracle on the prefill workload: all rows when they fit
     the time budget (they do on a 16-core host: ~3 s), else a seeded sample of
@@ -246,6 +281,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only-decode", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--no-multilayer", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (reference for the HBM byte counters)")
@@ -283,6 +319,7 @@ def main():
     pf = bench_prefill(args, torch, L, csa_inputs, R)
     dec = None if args.no_decode else bench_decode(args, torch, L, csa_inputs, R)
     att = None if args.no_attention else bench_attention(args, torch, L, csa_inputs, R)
+    mls = None if args.no_multilayer else bench_multilayer(args, torch, L, csa_inputs, R)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, R)
 
     p = pf["p"]
@@ -325,6 +362,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": dec,
         "attention": att,
+        "multilayer": mls,
         "peak_mem_bytes": pf["peak_mem"],
         "workspace_bytes": pf["ws"],
         "materialised_score_tensor_bytes": R.materialised_score_bytes(1, p["S_q"], p["H"], p["T"]),
