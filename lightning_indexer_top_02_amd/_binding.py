@@ -341,6 +341,7 @@ class MultiLayerSelector:
         self.overlap = bool(overlap)
         self.refreshes = 0
         self._cached = None
+        self._streams = []
 
     def select(self, step, layers, *, m=4, q_pos0=0, kv_len=None, causal=True):
         """layers: sequence of (q, k, w) indexer inputs, one per layer, sharing
@@ -353,7 +354,9 @@ class MultiLayerSelector:
         main = torch.cuda.current_stream()
         sels = []
         if self.overlap:
-            streams = [torch.cuda.Stream() for _ in layers]
+            while len(self._streams) < len(layers):      # created once, default priority
+                self._streams.append(torch.cuda.Stream())
+            streams = self._streams[: len(layers)]
             for s in streams:
                 s.wait_stream(main)
             for (q, k, w), s in zip(layers, streams):
