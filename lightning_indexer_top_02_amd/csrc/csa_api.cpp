@@ -38,6 +38,10 @@ csa_status ok() {
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// A dispatch counts work-items per grid dimension in 32 bits: one workgroup
+// per row of `threads` threads allows at most this many rows.
+long long max_rows_per_dispatch(int threads) { return ((1ll << 32) - 1) / threads; }
+
 bool env_is(const char* name, const char* val) {
   const char* e = std::getenv(name);
   return e && std::strcmp(e, val) == 0;
@@ -113,7 +117,10 @@ PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, ui
 }
 
 // Decode path: bf16, H=64, D=128, few query rows.
-bool decode_fast(const csa_problem* p) { return use_mfma(p) && p->S_q <= CSA_MAX_DECODE_SQ; }
+bool decode_fast(const csa_problem* p) {
+  return use_mfma(p) && p->S_q <= CSA_MAX_DECODE_SQ &&
+         (long long)p->B * p->S_q <= max_rows_per_dispatch(csa::DEC_SEL_THREADS);
+}
 
 struct DecodePlan {
   int nsplit, nbw;
@@ -159,6 +166,8 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
   if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
   const bool mfma = use_mfma(p);
   const bool sorted = (flags & CSA_SORTED) != 0;
+  if (sorted && (long long)p->B * p->S_q > max_rows_per_dispatch(256))
+    return fail(CSA_ERR_UNSUPPORTED, "CSA_SORTED supports at most %lld query rows", max_rows_per_dispatch(256));
   float* score_dst = out_score;
   if (sorted && !score_dst) score_dst = (float*)((char*)ws + pl.cand_bytes);
 
@@ -450,7 +459,7 @@ csa_status csa_union_rows(const int32_t* const* lists, const int32_t* widths, in
     if (rows < 0) return fail(CSA_ERR_INVALID, "rows=%lld < 0", (long long)rows);
     if (T < 1 || cap < 1) return fail(CSA_ERR_INVALID, "T and cap must be >= 1");
     if (T > CSA_MAX_UNION_T) return fail(CSA_ERR_UNSUPPORTED, "T=%d > %d", T, CSA_MAX_UNION_T);
-    if (rows > (1ll << 31) - 1) return fail(CSA_ERR_UNSUPPORTED, "too many rows");
+    if (rows > max_rows_per_dispatch(csa::UN_THREADS)) return fail(CSA_ERR_UNSUPPORTED, "too many rows");
     csa::UnionArgs a{};
     for (int i = 0; i < L; ++i) {
       if (widths[i] < 1) return fail(CSA_ERR_INVALID, "widths[%d]=%d < 1", i, widths[i]);
@@ -477,7 +486,7 @@ csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref,
     if (n_sel < 1 || n_ref < 1 || T < 1) return fail(CSA_ERR_INVALID, "n_sel, n_ref and T must be >= 1");
     if (n_ref > 8192) return fail(CSA_ERR_UNSUPPORTED, "n_ref=%d > 8192", n_ref);
     if (rows > 0 && (!sel || !ref || !out_recall)) return fail(CSA_ERR_INVALID, "sel, ref and out_recall must not be NULL");
-    if (rows > (1ll << 31) - 1) return fail(CSA_ERR_UNSUPPORTED, "too many rows");
+    if (rows > max_rows_per_dispatch(256)) return fail(CSA_ERR_UNSUPPORTED, "too many rows");
     hipError_t e = csa::launch_recall(sel, n_sel, ref, n_ref, rows, T, out_recall, (hipStream_t)hip_stream);
     if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "recall launch failed: %s", hipGetErrorString(e));
     return ok();

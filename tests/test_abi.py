@@ -216,3 +216,6 @@ def test_union_argument_errors(lib):
     assert call(widths=(4, 0)) == Bd.CSA_ERR_INVALID
     assert call(lists=(0x1000, 0)) == Bd.CSA_ERR_INVALID
     assert call(out=None) == Bd.CSA_ERR_INVALID
+    # one 1024-thread workgroup per row: a dispatch holds at most 2^32 work-items
+    assert call(rows=1 << 22) == Bd.CSA_ERR_UNSUPPORTED
+    assert lib.csa_set_recall(0x1000, 8, 0x2000, 8, 1 << 24, 100, 0x3000, None, 0, None) == Bd.CSA_ERR_UNSUPPORTED
