@@ -252,8 +252,12 @@ def cpu_baseline(seconds, R):
         what = f"the full workload: all {p['S_q']} query rows"
     else:
         n = int(max(8, seconds / per_row))
-        rows = np.sort(np.random.default_rng(77).choice(need_rows, size=min(n, len(need_rows)), replace=False))
-        what = f"{len(rows)} seeded random rows of the {len(need_rows)} that need a selection"
+        if n >= len(need_rows):
+            rows = need_rows
+            what = f"all {len(need_rows)} query rows that need a selection (the others only copy indices)"
+        else:
+            rows = np.sort(np.random.default_rng(77).choice(need_rows, size=n, replace=False))
+            what = f"{len(rows)} seeded random rows of the {len(need_rows)} that need a selection"
     t0 = time.perf_counter()
     oracle.oracle_topk(p, rows=rows)
     dt = time.perf_counter() - t0
