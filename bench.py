@@ -77,14 +77,23 @@ def _time_calls(torch, call, steps, warmup):
     return total_ms, sum(per) / len(per), per[len(per) // 2], per[0]
 
 
+def kernel_source_sha256():
+    """sha256 over the device sources (kernels and the headers they include),
+    in a fixed order: a traffic record applies only to the source it was
+    measured on."""
+    h = hashlib.sha256()
+    for f in ("csa_kernels.hip", "csa_device.hpp", "csa_internal.hpp"):
+        h.update(open(os.path.join(ROOT, "lightning_indexer_top_02_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def _traffic_record(kernel):
     """HBM bytes per launch measured by rocprofv3 counters, if recorded for the
     current kernel source (null once the kernel source changes)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "lightning_indexer_top_02_amd", "csrc", "csa_kernels.hip")
     try:
         rec = json.load(open(path)).get(kernel)
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_source_sha256()
         if rec and rec.get("src_sha256") == sha:
             return rec
     except (OSError, ValueError):

@@ -39,9 +39,6 @@ __device__ __forceinline__ u64 make_key(float s, uint32_t idx) {
 __device__ __forceinline__ int key_index(u64 key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 __device__ __forceinline__ float key_score(u64 key) { return order_bits_score((uint32_t)(key >> 32)); }
 
-// Smallest key whose score is >= s (any index).
-__device__ __forceinline__ u64 score_floor_key(float s) { return (u64)score_order_bits(s) << 32; }
-
 // ---------------------------------------------------------------- wave helpers
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -66,11 +63,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ void wave_own_stores_visible() {
   __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0) expcnt(7) lgkmcnt(15)
   asm volatile("" ::: "memory");
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_bcast(T v, int src) {
-  return __shfl(v, src, WAVE);
 }
 
 __device__ __forceinline__ u64 wave_min_u64(u64 v) {
@@ -252,7 +244,6 @@ __device__ __forceinline__ bool lin_bins_ok(float lo, float hi, LinBins& lb) {
 }
 
 constexpr int WAVE_LIST = 256;    // keys of one linear bin resolved by a wave from LDS
-constexpr int BLOCK_LIST = 512;
 
 struct AnyKey {
   __device__ __forceinline__ bool operator()(u64 v) const { return v != 0ull; }
@@ -341,56 +332,6 @@ struct ArrayKeys {
 template <int R, typename Pred>
 __device__ __forceinline__ u64 wave_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, Pred in) {
   return wave_radix_kth_at<R>(ArrayKeys<R>{x}, n, k, hist, in);
-}
-
-// Exact k-th largest of the n keys held in x (n > k >= 1): linear-bin
-// histogram, gather of the bin holding rank k into `list`, radix resolution;
-// the same steps as the streaming version below without any memory pass.
-// slo/shi: per-lane bounds on the scores in x (+inf/-inf where a lane has none).
-template <int R>
-__device__ __forceinline__ u64 wave_select_kth_regs(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* list,
-                                                    float slo, float shi) {
-  const int l = lane_id();
-  slo = wave_min_f32(slo);
-  shi = wave_max_f32(shi);
-  LinBins lb;
-  if (!lin_bins_ok(slo, shi, lb)) return wave_radix_kth(x, n, k, hist, AnyKey{});
-  wave_clear_hist(hist, SEL_BINS);
-  wave_lds_sync();
-#pragma unroll
-  for (int j = 0; j < R; ++j)
-    if (j * WAVE < n && x[j]) atomicAdd(&hist[lb(x[j])], 1u);
-  wave_lds_sync();
-  const BinPick pk = wave_pick_bin(hist, SEL_BINS, k);
-  wave_lds_sync();
-  const int r = k - pk.above;
-  const InBin inb{lb, pk.bin};
-  if (pk.count > WAVE_LIST) return wave_radix_kth(x, n, r, hist, inb);
-  int w = 0;
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const bool in = j * WAVE < n && inb(x[j]);
-    const u64 m = ballot(in);
-    if (in) list[w + lanes_below(m)] = x[j];
-    w += __popcll(m);
-  }
-  wave_lds_sync();
-  if (w <= WAVE) return wave_small_kth(list, w, r);
-  constexpr int RL = WAVE_LIST / WAVE;
-  u64 y[RL];
-#pragma unroll
-  for (int j = 0; j < RL; ++j) {
-    const int i = j * WAVE + l;
-    y[j] = i < w ? list[i] : 0ull;
-  }
-  wave_lds_sync();
-  if (w == r) {
-    u64 mn = ~0ull;
-#pragma unroll
-    for (int j = 0; j < RL; ++j) mn = (y[j] && y[j] < mn) ? y[j] : mn;
-    return wave_min_u64(mn);
-  }
-  return wave_radix_kth(y, w, r, hist, AnyKey{});
 }
 
 // The r-th largest of w distinct keys list[0..w) (1 <= r <= w <= WAVE_LIST).
@@ -520,144 +461,6 @@ __device__ __forceinline__ u64 wave_select_kth_stream(const u64* buf, int n, int
     return wave_min_u64(mn);
   }
   return wave_radix_kth(y, w, r, hist, AnyKey{});
-}
-
-// Block versions for the decode select: NT threads, R keys per thread in any
-// element layout (0 marks an empty slot).  hist: SEL_BINS entries; red: >= 2*NT/WAVE
-// u64; list: BLOCK_LIST u64; cnt: one int of LDS.
-template <int NT, int R, typename Pred>
-__device__ __forceinline__ u64 block_radix_kth(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* red, Pred in) {
-  const int tid = threadIdx.x;
-  const int l = lane_id(), wv = tid / WAVE;
-  constexpr int NW = NT / WAVE;
-  u64 lo = ~0ull, hi = 0ull;
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const u64 v = x[j];
-    if (in(v)) {
-      lo = v < lo ? v : lo;
-      hi = v > hi ? v : hi;
-    }
-  }
-  lo = wave_min_u64(lo);
-  hi = wave_max_u64(hi);
-  __syncthreads();
-  if (l == 0) { red[wv] = lo; red[NW + wv] = hi; }
-  __syncthreads();
-  lo = ~0ull; hi = 0ull;
-  for (int j = 0; j < NW; ++j) {
-    lo = red[j] < lo ? red[j] : lo;
-    hi = red[NW + j] > hi ? red[NW + j] : hi;
-  }
-  __syncthreads();
-  if (lo == hi) return lo;
-  int hi_bit = 64 - clz64(lo ^ hi);
-  u64 prefix = hi_bit >= 64 ? 0ull : (lo >> hi_bit);
-  int rank = k;
-  while (true) {
-    const int rb = hi_bit < SEL_RB ? hi_bit : SEL_RB;
-    const int shift = hi_bit - rb;
-    const int nb = 1 << rb;
-    const uint32_t dmask = (uint32_t)(nb - 1);
-    for (int b = tid; b < nb; b += NT) hist[b] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const u64 v = x[j];
-      const bool match = in(v) && (hi_bit >= 64 || (v >> hi_bit) == prefix);
-      if (match) atomicAdd(&hist[(uint32_t)(v >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    if (wv == 0) {
-      const BinPick pk = wave_pick_bin(hist, nb, rank);
-      if (l == 0) { red[0] = (u64)pk.bin; red[1] = (u64)pk.above; red[2] = (u64)pk.count; }
-    }
-    __syncthreads();
-    const int bin = (int)red[0], above = (int)red[1], cnt = (int)red[2];
-    __syncthreads();
-    rank -= above;
-    prefix = (prefix << rb) | (u64)bin;
-    hi_bit = shift;
-    if (cnt == rank || shift == 0) return prefix << shift;
-  }
-}
-
-template <int NT, int R>
-__device__ __forceinline__ u64 block_select_kth_regs(const u64 (&x)[R], int n, int k, uint32_t* hist, u64* red, u64* list,
-                                     int* cnt) {
-  const int tid = threadIdx.x;
-  const int l = lane_id(), wv = tid / WAVE;
-  constexpr int NW = NT / WAVE;
-  float slo = __builtin_inff(), shi = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    if (x[j]) {
-      const float s = key_score(x[j]);
-      slo = fminf(slo, s);
-      shi = fmaxf(shi, s);
-    }
-  }
-  slo = wave_min_f32(slo);
-  shi = wave_max_f32(shi);
-  float* fred = (float*)red;
-  __syncthreads();
-  if (l == 0) { fred[wv] = slo; fred[NW + wv] = shi; }
-  if (tid == 0) *cnt = 0;
-  __syncthreads();
-  slo = __builtin_inff(); shi = -__builtin_inff();
-  for (int j = 0; j < NW; ++j) {
-    slo = fminf(slo, fred[j]);
-    shi = fmaxf(shi, fred[NW + j]);
-  }
-  __syncthreads();
-  LinBins lb;
-  if (!lin_bins_ok(slo, shi, lb)) return block_radix_kth<NT>(x, n, k, hist, red, AnyKey{});
-  for (int b = tid; b < SEL_BINS; b += NT) hist[b] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    if (x[j]) atomicAdd(&hist[lb(x[j])], 1u);
-  }
-  __syncthreads();
-  if (wv == 0) {
-    const BinPick pk = wave_pick_bin(hist, SEL_BINS, k);
-    if (l == 0) { red[0] = (u64)pk.bin; red[1] = (u64)pk.above; red[2] = (u64)pk.count; }
-  }
-  __syncthreads();
-  const int bin = (int)red[0], r = k - (int)red[1], bcnt = (int)red[2];
-  __syncthreads();
-  const InBin inb{lb, bin};
-  if (bcnt > BLOCK_LIST) return block_radix_kth<NT>(x, n, r, hist, red, inb);
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    if (inb(x[j])) list[atomicAdd(cnt, 1)] = x[j];   // order within the bin is irrelevant
-  }
-  __syncthreads();
-  if (wv == 0) {
-    constexpr int RL = BLOCK_LIST / WAVE;
-    u64 y[RL];
-#pragma unroll
-    for (int j = 0; j < RL; ++j) {
-      const int i = j * WAVE + l;
-      y[j] = i < bcnt ? list[i] : 0ull;
-    }
-    u64 T;
-    if (bcnt <= WAVE) {
-      T = wave_small_kth(list, bcnt, r);
-    } else if (bcnt == r) {
-      u64 mn = ~0ull;
-#pragma unroll
-      for (int j = 0; j < RL; ++j) mn = (y[j] && y[j] < mn) ? y[j] : mn;
-      T = wave_min_u64(mn);
-    } else {
-      T = wave_radix_kth(y, bcnt, r, hist, AnyKey{});
-    }
-    if (l == 0) red[0] = T;
-  }
-  __syncthreads();
-  const u64 T = red[0];
-  __syncthreads();
-  return T;
 }
 
 // Block-level select over dense fp32 scores in global memory (implicit
