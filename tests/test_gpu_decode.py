@@ -112,10 +112,17 @@ def _select_case(case):
             k[b, s] = top
         p["k"] = csa_inputs.f32_to_bf16_bits(k)
         return p
+    if case == "noncausal":           # every key visible to every row, kv_len caps one sequence
+        p = csa_inputs.make_decode(B=3, context=4 * 6000, topk=700, n_planted=8, S_q=4, seed=57)
+        p["causal"] = False
+        p["q_pos0"] = 0                                  # causal rows would see almost nothing
+        p["kv_len"] = np.array([6000, 2500, 650], dtype=np.int32)
+        return p
     raise ValueError(case)
 
 
-@pytest.mark.parametrize("case", ["no_planted", "long_rows", "ragged_kv", "k_near_vis", "crowded_bin"])
+@pytest.mark.parametrize("case", ["no_planted", "long_rows", "ragged_kv", "k_near_vis", "crowded_bin",
+                                  "noncausal"])
 def test_decode_select_paths(case):
     p = _select_case(case)
     _say(f"decode select path case {case}: B={p['B']} S_q={p['S_q']} T={p['T']} k={p['topk']}")

@@ -17,7 +17,8 @@ from gpu_common import REL, FLOOR_DIV, check_exact, to_device  # noqa: E402
 def _thr(prob, cap, tau, bias, **kw):
     q, k, w, kv = to_device(prob)
     idx, cnt, sc = L.index_threshold_select(q, k, w, cap, prob_threshold=tau, logit_bias=bias, m=prob["m"],
-                                            q_pos0=prob["q_pos0"], kv_len=kv, return_scores=True, **kw)
+                                            q_pos0=prob["q_pos0"], kv_len=kv, return_scores=True,
+                                            causal=prob.get("causal", True), **kw)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), cnt.cpu().numpy(), sc.cpu().numpy()
 
@@ -98,12 +99,16 @@ def _decode_integer(B=3, S_q=2, T=3000, seed=31, kv_len=None):
                                                ("under_cap", 4096, 0.5, 0.0),     # every survivor fits
                                                ("high_threshold", 300, 0.5, -6.0),
                                                ("kv_len", 256, 0.5, 0.0),         # short and empty rows
-                                               ("long_rows", 1024, 0.5, 2.0)])    # rows past the register tile
+                                               ("long_rows", 1024, 0.5, 2.0),     # rows past the register tile
+                                               ("noncausal", 400, 0.5, 0.0)])
 def test_threshold_decode_path_exact(case, cap, tau, bias):
     if case == "kv_len":
         p = _decode_integer(kv_len=[3000, 170, 0])
     elif case == "long_rows":
         p = _decode_integer(B=2, S_q=1, T=40000, seed=32)
+    elif case == "noncausal":
+        p = _decode_integer(S_q=4, seed=33)
+        p["causal"], p["q_pos0"] = False, 0
     else:
         p = _decode_integer()
     ref_i, ref_c, ref_s = oracle.oracle_threshold(p, tau, bias, cap)
