@@ -380,13 +380,13 @@ struct AttnPlan {
   size_t opart_bytes, stat_bytes, total;
 };
 
-// Workgroups per query row: about 512 workgroups in all (two per CU), never
-// more than the row has 128-entry chunks.
+// Workgroups per query row: about 256 workgroups in all (one per CU), never
+// more than the row has AT_CHUNK-entry chunks.
 AttnPlan plan_attention(const csa_attn_problem* p, int n_sel) {
   AttnPlan pl;
   const long long rows = (long long)p->B * p->S_q;
   const int nchunk = (n_sel + csa::AT_CHUNK - 1) / csa::AT_CHUNK;
-  long long ns = (512 + rows - 1) / rows;
+  long long ns = (256 + rows - 1) / rows;
   ns = std::max(1ll, std::min(ns, (long long)nchunk));
   pl.nsplit = (int)ns;
   pl.opart_bytes = align_up((size_t)rows * pl.nsplit * csa::AT_H * csa::AT_D * sizeof(float));

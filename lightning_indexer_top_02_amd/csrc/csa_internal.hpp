@@ -67,8 +67,8 @@ constexpr int DEC_SEL_THREADS = 1024;
 
 // Sparse attention over selected keys (H = 64 heads, Dk = Dv = 128, bf16).
 constexpr int AT_H = 64, AT_D = 128;
-constexpr int AT_CHUNK = 128;          // selected keys per step of a workgroup
-constexpr int AT_THREADS = 256;
+constexpr int AT_CHUNK = 256;          // selected keys per step of a workgroup
+constexpr int AT_THREADS = 512;        // 8 waves: 32 keys each for the logits
 
 struct AttnArgs {
   const void* q;        // [rows][AT_H][AT_D] bf16

@@ -1011,11 +1011,12 @@ __device__ __forceinline__ uint32_t at_swz(int r, int col) {   // bf16 element (
   return (uint32_t)(r * AT_CHUNK * 2 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) << 1)));
 }
 
-__global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char ps[AT_H * AT_CHUNK * 2];      // P (bf16), head-major
   __shared__ __attribute__((aligned(16))) char vt[AT_D * AT_CHUNK * 2];      // V^T (bf16), dv-major
   __shared__ bf16x8 qs[2][8][WAVE];                                          // Q in MFMA A-operand order
-  __shared__ float red[4][AT_H];
+  constexpr int NWV = AT_THREADS / WAVE;
+  __shared__ float red[NWV][AT_H];
   __shared__ float mrun[AT_H], lrun[AT_H], mnew_s[AT_H], alpha_s[AT_H];
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.y, split = blockIdx.x, b = row / a.S_q;
@@ -1031,21 +1032,25 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
   auto entry = [&](int j) { return j < a.n_sel ? irow[j] : -1; };
   int ik = entry(split * AT_CHUNK + 32 * wv + (l & 31));
   int iv0 = entry(split * AT_CHUNK + 2 * (tid >> 2)), iv1 = entry(split * AT_CHUNK + 2 * (tid >> 2) + 1);
-  // the query operand goes to LDS (wave w copies slices 2w, 2w+1), which
-  // leaves registers for the key and value rows of a chunk in flight together;
-  // it is stored there once the first chunk's rows have been requested
-  bf16x8 qv[2][2];
+  // the query operand goes to LDS (wave w copies slice w of both head
+  // halves), which leaves registers for the key and value rows of a chunk in
+  // flight together; it is stored there once the first chunk's rows have been
+  // requested
+  static_assert(AT_THREADS / WAVE == 8, "one query slice per wave");
+  bf16x8 qv[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)row * AT_H + rt * 32 + (l & 31)) * AT_D);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) qv[rt][h] = src[2 * (2 * wv + h) + (l >> 5)];
+    qv[rt] = src[2 * wv + (l >> 5)];
   }
   if (tid < AT_H) {
     mrun[tid] = -__builtin_inff();
     lrun[tid] = 0.f;
   }
-  f32x16 o[2] = {f32x16{}, f32x16{}};                   // output columns 32w + (l & 31)
+  // P.V roles: wave w accumulates head tile rt = w % 2 for output columns
+  // 32 * (w / 2) .. + 31
+  const int prt = wv & 1, pdc = 32 * (wv >> 1);
+  f32x16 o = f32x16{};
   // head row of accumulator element e (rows of tile rt are rt*32 + this)
   auto hrow = [&](int e) { return 8 * (e >> 2) + 4 * (l >> 5) + (e & 3); };
 
@@ -1067,9 +1072,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
     }
     if (c == split) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) qs[rt][2 * wv + h][l] = qv[rt][h];
+      for (int rt = 0; rt < 2; ++rt) qs[rt][wv][l] = qv[rt];
     }
     __syncthreads();                                    // the query slices are in LDS (first chunk)
     f32x16 acc[2] = {f32x16{}, f32x16{}};
@@ -1105,7 +1108,9 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (tid < AT_H) {
-      const float cm = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+      float cm = red[0][tid];
+#pragma unroll
+      for (int j = 1; j < NWV; ++j) cm = fmaxf(cm, red[j][tid]);
       const float mo = mrun[tid], mn = fmaxf(mo, cm);
       mnew_s[tid] = mn;
       alpha_s[tid] = mn == -__builtin_inff() ? 1.f : __expf(mo - mn);
@@ -1157,23 +1162,21 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (tid < AT_H) {
-      lrun[tid] = alpha_s[tid] * lrun[tid] + (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
+      float cs = 0.f;
+#pragma unroll
+      for (int j = 0; j < NWV; ++j) cs += red[j][tid];
+      lrun[tid] = alpha_s[tid] * lrun[tid] + cs;
       mrun[tid] = mnew_s[tid];
     }
     // rescale this wave's output columns, then O += P . V over the chunk
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[rt][e] *= alpha_s[rt * 32 + hrow(e)];
+    for (int e = 0; e < 16; ++e) o[e] *= alpha_s[prt * 32 + hrow(e)];
 #pragma unroll
     for (int ks = 0; ks < AT_CHUNK / 16; ++ks) {
       const int kc = 16 * ks + 8 * (l >> 5);
-      const bf16x8 bv = *(const bf16x8*)(vt + at_swz(32 * wv + (l & 31), kc));
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8 ap = *(const bf16x8*)(ps + at_swz(rt * 32 + (l & 31), kc));
-        o[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bv, o[rt], 0, 0, 0);
-      }
+      const bf16x8 bv = *(const bf16x8*)(vt + at_swz(pdc + (l & 31), kc));
+      const bf16x8 ap = *(const bf16x8*)(ps + at_swz(prt * 32 + (l & 31), kc));
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap, bv, o, 0, 0, 0);
     }
     const int cn = c + a.nsplit;                        // the next chunk's entries
     ik = entry(cn * AT_CHUNK + 32 * wv + (l & 31));
@@ -1184,9 +1187,7 @@ __global__ __launch_bounds__(AT_THREADS, 2) void attn_chunk_kernel(AttnArgs a) {
   const size_t pr = (size_t)row * a.nsplit + split;
   float* op = a.opart + pr * AT_H * AT_D;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) op[(size_t)(rt * 32 + hrow(e)) * AT_D + 32 * wv + (l & 31)] = o[rt][e];
+  for (int e = 0; e < 16; ++e) op[(size_t)(prt * 32 + hrow(e)) * AT_D + pdc + (l & 31)] = o[e];
   if (tid < AT_H) {
     a.mpart[pr * AT_H + tid] = mrun[tid];
     a.lpart[pr * AT_H + tid] = lrun[tid];

@@ -176,9 +176,9 @@ def test_attention_struct_layout():
 
 def test_attention_workspace_size(lib):
     n = ctypes.c_size_t(0)
-    # 32 rows, 16 chunks of 128 entries -> 16 workgroups per row
+    # 32 rows, 8 chunks of 256 entries -> 8 workgroups per row
     assert lib.csa_attention_workspace_size(ctypes.byref(_attn_prob()), 2048, ctypes.byref(n)) == 0
-    assert n.value == 32 * 16 * 64 * 128 * 4 + 2 * (32 * 16 * 64 * 4)
+    assert n.value == 32 * 8 * 64 * 128 * 4 + 2 * (32 * 8 * 64 * 4)
     # many rows: one workgroup per row
     assert lib.csa_attention_workspace_size(ctypes.byref(_attn_prob(B=4, S_q=512)), 2048, ctypes.byref(n)) == 0
     assert n.value == 2048 * 64 * 128 * 4 + 2 * (2048 * 64 * 4)

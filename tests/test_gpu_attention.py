@@ -58,15 +58,15 @@ def _check(p, o, rows=None):
 @pytest.mark.parametrize("case", ["ragged_chunks", "short_rows", "many_rows", "invalid_entries",
                                   "chunks_per_workgroup"])
 def test_attention_matches_oracle(case):
-    if case == "ragged_chunks":        # 3 chunks of 128, 128 and 44 entries; -1 padding at the end
+    if case == "ragged_chunks":        # chunks of 256 and 44 entries; -1 padding at the end
         p = csa_inputs.make_attention(2, 3, 1000, n_sel=300, seed=11, pad=10)
     elif case == "short_rows":         # fewer entries than one chunk
         p = csa_inputs.make_attention(3, 2, 500, n_sel=37, seed=12)
     elif case == "many_rows":          # more rows than workgroups: one workgroup per row
         p = csa_inputs.make_attention(2, 160, 700, n_sel=200, seed=13, pad=3)
-    elif case == "chunks_per_workgroup":  # 600 rows -> one workgroup per row walks all 4 chunks
-        p = csa_inputs.make_attention(2, 300, 2000, n_sel=400, seed=18, pad=7)
-        p["idx"][1, 5, :200] = -1                                        # first chunks of a row empty
+    elif case == "chunks_per_workgroup":  # 600 rows -> one workgroup per row walks all 3 chunks
+        p = csa_inputs.make_attention(2, 300, 2000, n_sel=700, seed=18, pad=7)
+        p["idx"][1, 5, :300] = -1                                        # first chunk of a row empty
     else:                              # entries >= T and < -1 are skipped like -1
         p = csa_inputs.make_attention(2, 2, 400, n_sel=260, seed=14)
         p["idx"][0, 0, ::7] = 400 + np.arange(len(p["idx"][0, 0, ::7]), dtype=np.int32)
