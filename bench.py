@@ -240,7 +240,7 @@ def bench_multilayer(args, torch, L, csa_inputs, R):
                 frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_refresh=nbytes, refreshes=steps,
                 refresh_interval_steps=64,
                 workload="3 indexer layers x decode B=32, T=32768, H_I=64, d_I=128; threshold tau=0.5, cap 2048; "
-                         "OR-union (cap 6144)")
+                         "OR-union (cap 6144); the three layers selected in one batched launch")
 
 
 def cpu_baseline(seconds, R):

@@ -188,6 +188,21 @@ csa_status csa_attention_workspace_size(const csa_attn_problem* prob, int32_t n_
 csa_status csa_sparse_attention(const csa_attn_problem* prob, const int32_t* idx, int32_t n_sel, float scale,
                                 float* out, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* The threshold selection of several problems of one shape at once (one
+ * problem per indexer layer, as in multi-layer selection below): problem i is
+ * probs[i], with its results in out_idx[i] [B, S_q, cap] and out_count[i]
+ * [B, S_q] (optional out_score[i], or out_score NULL).  probs, out_idx,
+ * out_count and out_score are HOST arrays of L entries; 1 <= L <=
+ * CSA_MAX_UNION_LISTS.  Same results as L calls of csa_index_threshold_select;
+ * the problems run in one launch of each decode kernel, so this form requires
+ * what that path requires of every problem (bf16, H=64, D=128, S_q <=
+ * CSA_MAX_DECODE_SQ) and equal B, S_q and T (CSA_ERR_UNSUPPORTED otherwise).
+ * ws: L times csa_workspace_size(CSA_OP_THRESHOLD, probs[0], cap, ...) bytes. */
+csa_status csa_index_threshold_select_layers(const csa_problem* const* probs, int32_t L, float prob_threshold,
+                                             float logit_bias, int32_t cap, uint32_t flags, int32_t* const* out_idx,
+                                             int32_t* const* out_count, float* const* out_score, void* ws,
+                                             size_t ws_bytes, void* hip_stream);
+
 /* Union of several selections per row (multi-layer selection: the
  * FlashMemory-DeepSeek-V4 review, "What carries the argument", places its
  * Memory Indexer on three layers and combines their keep decisions with a

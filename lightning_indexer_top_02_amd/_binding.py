@@ -60,6 +60,9 @@ _SIGS = {
     "csa_index_topk_prefill": (_i32, [_P, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_decode": (_i32, [_P, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_threshold_select": (_i32, [_P, _f32, _f32, _i32, _u32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_threshold_select_layers": (_i32, [ctypes.POINTER(_P), _i32, _f32, _f32, _i32, _u32,
+                                                 ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                 _vp, _sz, _vp]),
     "csa_index_topk_interleaved": (_i32, [_P, _i32, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
     "csa_set_recall": (_i32, [_vp, _i32, _vp, _i32, ctypes.c_int64, _i32, _vp, _vp, _sz, _vp]),
     "csa_attention_workspace_size": (_i32, [_PA, _i32, ctypes.POINTER(_sz)]),
@@ -226,6 +229,52 @@ def index_threshold_select(q, k, w, cap, *, prob_threshold=0.5, logit_bias=0.0, 
     return (idx, cnt, sc) if sc is not None else (idx, cnt)
 
 
+MAX_LAYERS = 8
+
+
+def batchable_layers(layers) -> bool:
+    """True when index_threshold_select_layers takes these (q, k, w) layers:
+    at most MAX_LAYERS, all bf16 with H=64, D=128, S_q <= MAX_DECODE_SQ, and
+    the same B, S_q and T."""
+    torch = _torch()
+    if not 1 <= len(layers) <= MAX_LAYERS:
+        return False
+    q0, k0, _ = layers[0]
+    for q, k, w in layers:
+        if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+            return False
+        if q.dim() != 4 or k.dim() != 3 or q.shape[2] != 64 or q.shape[3] != 128 or q.shape[1] > MAX_DECODE_SQ:
+            return False
+        if q.shape[:2] != q0.shape[:2] or k.shape[1] != k0.shape[1]:
+            return False
+    return True
+
+
+def index_threshold_select_layers(layers, cap, *, prob_threshold=0.5, logit_bias=0.0, m=4, q_pos0=0, kv_len=None,
+                                  sorted=False, causal=True, workspace=None):
+    """index_threshold_select over several same-shape decode problems
+    (layers: sequence of (q, k, w)) in one launch per kernel; returns a list
+    of (idx [B,S_q,cap], count [B,S_q]), one per layer."""
+    torch = _torch()
+    if not batchable_layers(layers):
+        raise ValueError("layers must be 1..8 bf16 decode problems (H=64, D=128, S_q<=16) of one shape")
+    probs = [make_problem(q, k, w, m, q_pos0, kv_len) for q, k, w in layers]
+    flags = _flags(sorted, causal)
+    B, S_q = layers[0][0].shape[:2]
+    dev = layers[0][0].device
+    idx = [torch.empty((B, S_q, cap), dtype=torch.int32, device=dev) for _ in layers]
+    cnt = [torch.empty((B, S_q), dtype=torch.int32, device=dev) for _ in layers]
+    n = len(layers)
+    ws = _workspace(n * workspace_size(OP_THRESHOLD, probs[0], cap, 1, flags), dev, workspace)
+    pp = (_P * n)(*[ctypes.pointer(p) for p in probs])
+    pi = (_vp * n)(*[_ptr(t) for t in idx])
+    pc = (_vp * n)(*[_ptr(t) for t in cnt])
+    _check(load_library().csa_index_threshold_select_layers(pp, n, float(prob_threshold), float(logit_bias),
+                                                            int(cap), flags, pi, pc, None, _ptr(ws), _nbytes(ws),
+                                                            _stream_handle()))
+    return list(zip(idx, cnt))
+
+
 def index_topk_interleaved(q, k, w, P, k_local, *, m=4, q_pos0=0, kv_len=None, sorted=False, causal=True,
                            return_scores=False, out=None, workspace=None):
     """Per-partition (s mod P) local top-k_local: int32 [B, S_q, P*k_local]."""
@@ -328,17 +377,21 @@ class MultiLayerSelector:
     """OR-union of several indexer layers' threshold selections, recomputed
     every `tau` decode steps and reused in between (FlashMemory-DeepSeek-V4
     review: Memory Indexer on three layers, keep decisions OR-ed, a decode
-    trigger interval of 64 steps).  Each layer's selection may run on its own
-    HIP stream (`overlap=True`), joined before the union on the caller's
-    current stream.  All compute is in the library's kernels."""
+    trigger interval of 64 steps).  Same-shape decode layers are selected in
+    one batched launch (`batched=True`); otherwise each layer's selection runs
+    in turn, or on its own HIP stream (`overlap=True`), joined before the
+    union on the caller's current stream.  All compute is in the library's
+    kernels."""
 
-    def __init__(self, tau=64, prob_threshold=0.5, logit_bias=0.0, cap=2048, union_cap=None, overlap=False):
+    def __init__(self, tau=64, prob_threshold=0.5, logit_bias=0.0, cap=2048, union_cap=None, overlap=False,
+                 batched=True):
         self.tau = int(tau)
         self.prob_threshold = float(prob_threshold)
         self.logit_bias = float(logit_bias)
         self.cap = int(cap)
         self.union_cap = int(union_cap) if union_cap is not None else None
         self.overlap = bool(overlap)
+        self.batched = bool(batched)
         self.refreshes = 0
         self._cached = None
         self._streams = []
@@ -353,7 +406,11 @@ class MultiLayerSelector:
         ucap = self.union_cap if self.union_cap is not None else min(T, self.cap * len(layers))
         main = torch.cuda.current_stream()
         sels = []
-        if self.overlap:
+        if self.batched and batchable_layers(layers):
+            sels = [idx for idx, _ in index_threshold_select_layers(
+                layers, self.cap, prob_threshold=self.prob_threshold, logit_bias=self.logit_bias, m=m,
+                q_pos0=q_pos0, kv_len=kv_len, causal=causal)]
+        elif self.overlap:
             while len(self._streams) < len(layers):      # created once, default priority
                 self._streams.append(torch.cuda.Stream())
             streams = self._streams[: len(layers)]

@@ -250,6 +250,21 @@ csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap,
 
 namespace {
 
+// sigma(I + bias) > tau  <=>  I > theta = log(tau/(1-tau)) - bias, decided on the
+// fp32 score: I > theta  <=>  I >= f, f = the smallest float above theta; the
+// selection key of f with any index is the smallest surviving key.
+unsigned long long threshold_key(float prob_threshold, float logit_bias) {
+  const double t = (double)prob_threshold;
+  const double theta = std::log(t / (1.0 - t)) - (double)logit_bias;
+  float f = (float)theta;
+  if ((double)f <= theta) f = std::nextafter(f, INFINITY);
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (unsigned long long)ord << 32;
+}
+
 // Decode-shaped problems (bf16, H=64, D=128, S_q <= CSA_MAX_DECODE_SQ): the
 // key scan, then the per-row select; thr != 0 selects threshold mode
 // (survivors = keys >= thr, counted into out_count, the best kk written).
@@ -333,21 +348,75 @@ csa_status csa_index_threshold_select(const csa_problem* prob, float prob_thresh
     if (!(prob_threshold > 0.0f && prob_threshold < 1.0f))
       return fail(CSA_ERR_INVALID, "prob_threshold must be in (0,1)");
     if (!std::isfinite(logit_bias)) return fail(CSA_ERR_INVALID, "logit_bias must be finite");
-    // sigma(I + bias) > tau  <=>  I > theta = log(tau/(1-tau)) - bias, decided on the
-    // fp32 score: I > theta  <=>  I >= f, f = the smallest float above theta.
-    const double t = (double)prob_threshold;
-    const double theta = std::log(t / (1.0 - t)) - (double)logit_bias;
-    float f = (float)theta;
-    if ((double)f <= theta) f = std::nextafter(f, INFINITY);
-    uint32_t u;
-    std::memcpy(&u, &f, 4);
-    if (u == 0x80000000u) u = 0u;
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    const unsigned long long thr = (unsigned long long)ord << 32;
+    const unsigned long long thr = threshold_key(prob_threshold, logit_bias);
     if (decode_fast(prob))                            // few query rows: the decode key scan and select
       return run_decode(prob, cap, flags, thr, out_idx, out_score, out_count, ws, ws_bytes, hip_stream);
     return run_prefill_family(prob, csa::MODE_THRESHOLD, cap, 1, flags, thr, out_idx, out_score, out_count, ws,
                               ws_bytes, hip_stream);
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
+static_assert(csa::DEC_MAX_BATCH == CSA_MAX_UNION_LISTS, "layer batch and union list limits agree");
+
+csa_status csa_index_threshold_select_layers(const csa_problem* const* probs, int32_t L, float prob_threshold,
+                                             float logit_bias, int32_t cap, uint32_t flags, int32_t* const* out_idx,
+                                             int32_t* const* out_count, float* const* out_score, void* ws,
+                                             size_t ws_bytes, void* hip_stream) {
+  try {
+    if (L < 1 || L > csa::DEC_MAX_BATCH) return fail(CSA_ERR_INVALID, "L=%d outside [1, %d]", L, csa::DEC_MAX_BATCH);
+    if (!probs || !out_idx || !out_count) return fail(CSA_ERR_INVALID, "probs, out_idx and out_count must not be NULL");
+    csa_status s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(cap, "cap")) != CSA_OK) return s;
+    if (!(prob_threshold > 0.0f && prob_threshold < 1.0f))
+      return fail(CSA_ERR_INVALID, "prob_threshold must be in (0,1)");
+    if (!std::isfinite(logit_bias)) return fail(CSA_ERR_INVALID, "logit_bias must be finite");
+    for (int i = 0; i < L; ++i) {
+      if ((s = validate_problem(probs[i])) != CSA_OK) return s;
+      if (!out_idx[i] || !out_count[i]) return fail(CSA_ERR_INVALID, "out_idx[%d] and out_count[%d] must not be NULL", i, i);
+      if (!decode_fast(probs[i])) return fail(CSA_ERR_UNSUPPORTED, "problem %d is not decode-shaped (bf16, H=64, D=128, S_q<=%d)", i, CSA_MAX_DECODE_SQ);
+      if (probs[i]->B != probs[0]->B || probs[i]->S_q != probs[0]->S_q || probs[i]->T != probs[0]->T)
+        return fail(CSA_ERR_UNSUPPORTED, "problems must share B, S_q and T");
+    }
+    const DecodePlan d = plan_decode(probs[0], cap, flags);
+    const size_t need = d.total * (size_t)L;
+    if (ws_bytes < need || !ws) return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
+    const unsigned long long thr = threshold_key(prob_threshold, logit_bias);
+    const bool sorted = (flags & CSA_SORTED) != 0;
+    csa::DecodeBatch bt{};
+    bt.L = L;
+    float* score_dst[csa::DEC_MAX_BATCH];
+    for (int i = 0; i < L; ++i) {
+      const csa_problem* p = probs[i];
+      char* wp = (char*)ws + d.total * i;
+      score_dst[i] = out_score ? out_score[i] : nullptr;
+      if (sorted && !score_dst[i]) score_dst[i] = (float*)(wp + d.score_bytes + d.bound_bytes);
+      csa::DecodeArgs& a = bt.a[i];
+      a.q = p->q; a.k = p->k; a.w = p->w; a.kv_len = p->kv_len;
+      a.B = p->B; a.S_q = p->S_q; a.T = p->T; a.m = p->m; a.q_pos0 = p->q_pos0;
+      a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
+      a.thr_fixed = thr;
+      a.out_count = out_count[i];
+      a.scores = (float*)wp;
+      a.bounds = (uint4*)(wp + d.score_bytes);
+      a.nbw = d.nbw;
+      a.kk = cap;
+      a.out_idx = out_idx[i];
+      a.out_score = score_dst[i];
+    }
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = csa::launch_decode_batch(bt, d.nsplit, st);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+    if (sorted) {
+      for (int i = 0; i < L; ++i) {
+        e = csa::launch_sort_rows(out_idx[i], score_dst[i], (long long)probs[0]->B * probs[0]->S_q, cap, st);
+        if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "sort launch failed: %s", hipGetErrorString(e));
+      }
+    }
+    return ok();
   } catch (...) {
     return fail(CSA_ERR_INVALID, "internal error");
   }

@@ -59,6 +59,13 @@ struct DecodeArgs {
   float* out_score;
 };
 
+// Up to 8 decode problems of one shape (B, S_q, T) launched together.
+constexpr int DEC_MAX_BATCH = 8;
+struct DecodeBatch {
+  DecodeArgs a[DEC_MAX_BATCH];
+  int L;
+};
+
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_CHUNK = 1024;        // keys per decode-scan workgroup
 constexpr int DEC_RING = 3;            // key-row buffers per wave in the decode scan
@@ -108,6 +115,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, h
 // Resident workgroups per CU of the chosen prefill kernel (>= 1).
 int prefill_blocks_per_cu(int mode, bool mfma, bool bf16);
 hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st);
+hipError_t launch_decode_batch(const DecodeBatch& bt, int nsplit, hipStream_t st);
 hipError_t launch_sort_rows(int32_t* idx, float* score, long long rows, int len, hipStream_t st);
 hipError_t launch_recall(const int32_t* sel, int n_sel, const int32_t* ref, int n_ref,
                          long long rows, int T, float* out, hipStream_t st);

@@ -599,7 +599,7 @@ __device__ __forceinline__ int decode_visible(const DecodeArgs& a, int b, int i)
   return (int)v;
 }
 
-__global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.y, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
@@ -714,6 +714,13 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs
   }
 }
 
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs a) { decode_score_body(a); }
+
+// Several problems of one shape in one launch (grid z = problem).
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_batch_kernel(DecodeBatch bt) {
+  decode_score_body(bt.a[blockIdx.z]);
+}
+
 // decode_select: one workgroup per query row; exact top-kk of the row's
 // dense scores.  Wave w holds the contiguous element range [w*2048, w*2048+2048)
 // in registers (element w*2048 + j*64 + lane in v[j]).
@@ -765,7 +772,7 @@ __device__ __forceinline__ bool row_bins_ok(uint32_t lo_bits, uint32_t hi_bits, 
   return lin_bins_ok(lo, hi, rb.lin);
 }
 
-__global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
   constexpr int NW = DEC_SEL_THREADS / WAVE;
   __shared__ __attribute__((aligned(16))) uint32_t hist[SEL_BINS];
   __shared__ u64 red[2 * NW];
@@ -975,6 +982,12 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeAr
     oi[e] = -1;
     if (os) os[e] = -__builtin_inff();
   }
+}
+
+__global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_kernel(DecodeArgs a) { decode_select_body(a); }
+
+__global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_batch_kernel(DecodeBatch bt) {
+  decode_select_body(bt.a[blockIdx.z]);
 }
 
 // ============================================================ sparse attention
@@ -1422,6 +1435,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, h
     case MODE_THRESHOLD: launch_prefill_mode<MODE_THRESHOLD>(a, mfma, grid, st); break;
     default: launch_prefill_mode<MODE_INTERLEAVED>(a, mfma, grid, st); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_batch(const DecodeBatch& bt, int nsplit, hipStream_t st) {
+  const DecodeArgs& a = bt.a[0];
+  decode_score_batch_kernel<<<dim3(nsplit, a.B * a.S_q, bt.L), DEC_THREADS, 0, st>>>(bt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_select_batch_kernel<<<dim3(a.B * a.S_q, 1, bt.L), DEC_SEL_THREADS, 0, st>>>(bt);
   return hipGetLastError();
 }
 

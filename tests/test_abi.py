@@ -219,3 +219,29 @@ def test_union_argument_errors(lib):
     # one 1024-thread workgroup per row: a dispatch holds at most 2^32 work-items
     assert call(rows=1 << 22) == Bd.CSA_ERR_UNSUPPORTED
     assert lib.csa_set_recall(0x1000, 8, 0x2000, 8, 1 << 24, 100, 0x3000, None, 0, None) == Bd.CSA_ERR_UNSUPPORTED
+
+
+def test_threshold_layers_argument_errors(lib):
+    def call(probs, L=None, tau=0.5, cap=64, idx=None, cnt=None, ws=0x7000, ws_bytes=1 << 40):
+        n = len(probs)
+        PP = (ctypes.POINTER(Bd.CsaProblem) * max(n, 1))(*[ctypes.pointer(p) for p in probs])
+        V = ctypes.c_void_p * max(n, 1)
+        I = V(*(idx if idx is not None else [0x4000 + 0x100 * i for i in range(n)]))
+        C = V(*(cnt if cnt is not None else [0x8000 + 0x100 * i for i in range(n)]))
+        return lib.csa_index_threshold_select_layers(PP, n if L is None else L, tau, 0.0, cap, 0, I, C, None, ws,
+                                                     ws_bytes, None)
+    dec = lambda **kw: _prob(S_q=1, **kw)            # noqa: E731
+    assert call([dec(), dec()], L=0) == Bd.CSA_ERR_INVALID
+    assert call([dec()] * 9) == Bd.CSA_ERR_INVALID
+    assert call([dec(), dec()], tau=1.0) == Bd.CSA_ERR_INVALID
+    assert call([dec(), dec()], cap=0) == Bd.CSA_ERR_INVALID
+    assert call([dec(), dec(B=0)]) == Bd.CSA_ERR_INVALID
+    assert call([dec(), dec()], cnt=[0x8000, 0]) == Bd.CSA_ERR_INVALID
+    assert call([dec(), _prob(S_q=17)]) == Bd.CSA_ERR_UNSUPPORTED      # not decode-shaped
+    assert call([dec(), dec(T=300)]) == Bd.CSA_ERR_UNSUPPORTED         # shapes differ
+    assert call([dec(), dec(B=2)]) == Bd.CSA_ERR_UNSUPPORTED
+    assert call([dec(), dec()], ws_bytes=16) == Bd.CSA_ERR_WORKSPACE
+    assert call([dec(), dec()], ws=0x7004) == Bd.CSA_ERR_INVALID
+    # the workspace is the per-layer threshold workspace times the layer count
+    n1 = L.workspace_size(L.OP_THRESHOLD, dec(), 64, 1, 0)
+    assert call([dec(), dec(), dec()], ws_bytes=3 * n1 - 1) == Bd.CSA_ERR_WORKSPACE

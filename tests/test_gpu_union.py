@@ -48,13 +48,14 @@ def _dev(p):
     return q, k, torch.from_numpy(p["w"]).cuda()
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_multilayer_union_and_refresh(overlap):
+@pytest.mark.parametrize("mode", ["batched", "sequential", "overlap"])
+def test_multilayer_union_and_refresh(mode):
     probs = [_layer(s) for s in (21, 22, 23)]
     layers = [_dev(p) for p in probs]
     cap, ucap = 96, 320
-    sel = L.MultiLayerSelector(tau=4, prob_threshold=0.5, cap=cap, union_cap=ucap, overlap=overlap)
-    _say(f"multi-layer union, overlap={overlap}")
+    sel = L.MultiLayerSelector(tau=4, prob_threshold=0.5, cap=cap, union_cap=ucap, overlap=mode == "overlap",
+                               batched=mode == "batched")
+    _say(f"multi-layer union, mode={mode}")
     u, c = sel.select(0, layers, m=4, q_pos0=probs[0]["q_pos0"])
     torch.cuda.synchronize()
     ref, rcnt = oracle.oracle_multilayer(probs, 0.5, cap, ucap)
@@ -66,3 +67,30 @@ def test_multilayer_union_and_refresh(overlap):
     u2, _ = sel.select(4, layers, m=4, q_pos0=probs[0]["q_pos0"])
     torch.cuda.synchronize()
     assert sel.refreshes == 2 and (u2.cpu().numpy() == ref).all()
+
+
+@pytest.mark.parametrize("case", ["integer", "decode_workload"])
+def test_batched_threshold_matches_per_layer(case):
+    """One batched launch over the layers gives, layer by layer, exactly the
+    indices and counts of separate csa_index_threshold_select calls."""
+    if case == "integer":                       # ragged kv_len, non-causal, cap below some counts
+        probs = [_layer(s, S_q=5, T=900) for s in (31, 32, 33, 34)]
+        layers = [_dev(p) for p in probs]
+        kv = torch.tensor([900, 517], dtype=torch.int32).cuda()
+        kw = dict(m=4, q_pos0=0, kv_len=kv, causal=False)
+        cap, tau = 40, 0.5
+    else:                                       # three layers at B=32, T=32768, cap 2048
+        pd = [csa_inputs.make_decode(seed=s) for s in (1007, 1008, 1009)]
+        layers = [(torch.from_numpy(p["q"].view(np.int16)).view(torch.bfloat16).cuda(),
+                   torch.from_numpy(p["k"].view(np.int16)).view(torch.bfloat16).cuda(),
+                   torch.from_numpy(p["w"]).cuda()) for p in pd]
+        kw = dict(m=pd[0]["m"], q_pos0=pd[0]["q_pos0"])
+        cap, tau = 2048, 0.5
+    _say(f"batched threshold selection, case {case}, {len(layers)} layers")
+    got = L.index_threshold_select_layers(layers, cap, prob_threshold=tau, **kw)
+    for (q, k, w), (gi, gc) in zip(layers, got):
+        ri, rc = L.index_threshold_select(q, k, w, cap, prob_threshold=tau, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(gc, rc)
+        a, b = gi.cpu().numpy(), ri.cpu().numpy()
+        assert (np.sort(a, axis=-1) == np.sort(b, axis=-1)).all()
