@@ -16,7 +16,9 @@ Also reported on the same JSON line:
   attention     sparse attention over 2048 selected of T=32768 entries for the
                 same 32 rows (64 heads, d=128) in GB/s against HBM peak;
   multilayer    one refresh of a three-layer threshold selection with OR-union
-                at the decode shape, in GB/s of indexer keys against HBM peak;
+                at the decode shape, in GB/s of indexer keys against HBM peak,
+                and a three-layer stack with previous-layer reuse (indexer
+                top-k plus sparse attention per layer);
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50]
@@ -234,13 +236,49 @@ def bench_multilayer(args, torch, L, csa_inputs, R):
     ms = total_ms / steps
     gbps = nbytes / (ms * 1e-3) / 1e9
     _log(f"multi-layer refresh: {ms * 1e3:.1f} us per refresh, {gbps:.0f} GB/s")
+    res = dict(value=round(gbps, 1), unit="GB/s", ms_per_refresh=round(ms, 5),
+               frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_refresh=nbytes, refreshes=steps,
+               refresh_interval_steps=64,
+               workload="3 indexer layers x decode B=32, T=32768, H_I=64, d_I=128; threshold tau=0.5, cap 2048; "
+                        "OR-union (cap 6144); the three layers selected in one batched launch")
+    if not args.no_mli:
+        res["previous_layer_reuse"] = _bench_mli(args, torch, L, R, layers, p)
     del layers, sel
     torch.cuda.empty_cache()
-    return dict(value=round(gbps, 1), unit="GB/s", ms_per_refresh=round(ms, 5),
-                frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_refresh=nbytes, refreshes=steps,
-                refresh_interval_steps=64,
-                workload="3 indexer layers x decode B=32, T=32768, H_I=64, d_I=128; threshold tau=0.5, cap 2048; "
-                         "OR-union (cap 6144); the three layers selected in one batched launch")
+    return res
+
+
+def _bench_mli(args, torch, L, R, ind_layers, p):
+    """Previous-layer reuse over the same three indexer layers, each with its
+    own attention K/V (B=32, T=32768, 64 heads, d=128, top-2048): layer 0 runs
+    its indexer then attends; layer 1 attends over layer 0's selection while
+    layer 1's indexer runs (for layer 2); layer 2 attends over layer 1's.
+    Timed on one stream and with the indexer on a second stream."""
+    g = torch.Generator(device="cuda").manual_seed(1010)
+    layers = []
+    for ind in ind_layers:
+        B, T = ind[1].shape[0], ind[1].shape[1]
+        att = tuple(torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+                    for shape in ((B, 1, 64, 128), (B, T, 128), (B, T, 128)))
+        layers.append((ind, att))
+    out = {}
+    for ov in (False, True):
+        mli = L.MultiLayerIndexer(topk=2048, overlap=ov)
+
+        def call(_):
+            mli.run(layers, m=p["m"], q_pos0=p["q_pos0"])
+        total_ms, _, _, _ = _time_calls(torch, call, max(args.steps // 2, 20), min(args.warmup, 10))
+        out["ms_per_stack_overlap" if ov else "ms_per_stack"] = round(total_ms / max(args.steps // 2, 20), 5)
+    nbytes = 2 * R.decode_bytes(p["B"], 1, p["T"], p["H"], p["D"], 2048) + \
+        3 * R.attention_bytes(p["B"], p["B"] * 2048, 64, 128, 128, 2048)
+    ms = out["ms_per_stack"]
+    _log(f"previous-layer reuse, 3 layers: {ms * 1e3:.1f} us per stack (indexer on a second stream: "
+         f"{out['ms_per_stack_overlap'] * 1e3:.1f} us)")
+    del layers
+    return dict(value=round(nbytes / (ms * 1e-3) / 1e9, 1), unit="GB/s", bytes_per_stack=nbytes,
+                frac_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / R.PEAK_HBM_GBPS, 4), **out,
+                workload="3 layers: indexer top-2048 (B=32, T=32768) for layers 0 and 1, sparse attention "
+                         "(64 heads, d=128) for layers 0-2 over the previous layer's selection")
 
 
 def cpu_baseline(seconds, R):
@@ -295,6 +333,7 @@ def main():
     ap.add_argument("--only-decode", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-multilayer", action="store_true")
+    ap.add_argument("--no-mli", action="store_true", help="skip the previous-layer reuse timing")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (reference for the HBM byte counters)")

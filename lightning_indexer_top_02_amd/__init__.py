@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     index_threshold_select, index_topk_decode, index_topk_interleaved, index_topk_prefill,
     load_library, make_problem, set_recall, version, workspace_size,
     CsaAttnProblem, attention_workspace_size, make_attn_problem, sparse_attention, union_rows,
-    MultiLayerSelector, MAX_LAYERS, batchable_layers, index_threshold_select_layers,
+    MultiLayerSelector, MAX_LAYERS, batchable_layers, index_threshold_select_layers, MultiLayerIndexer,
 )

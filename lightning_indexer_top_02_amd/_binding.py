@@ -434,3 +434,54 @@ class MultiLayerSelector:
         self._cached = union_rows(sels, T, ucap)
         self.refreshes += 1
         return self._cached
+
+
+def _topk_any(q, k, w, topk, **kw):
+    """Top-k through the decode entry for decode-shaped rows, else prefill."""
+    if q.shape[1] <= MAX_DECODE_SQ:
+        return index_topk_decode(q, k, w, topk, **kw)
+    return index_topk_prefill(q, k, w, topk, **kw)
+
+
+class MultiLayerIndexer:
+    """Previous-layer reuse across a stack of sparse-attention layers
+    (Multi-layer Indexer post, "MLI"): layer l >= 1 attends to the top-k that
+    layer l-1's indexer picked, while layer l's own indexer runs on a second
+    HIP stream to serve layer l+1 (`overlap=True`); layer 0 runs its own
+    indexer before its attention.  By default the same schedule is issued on
+    the caller's stream alone (identical results): at B=32, T=32768 the scan
+    fills every CU, so a concurrent attention only waits for it and the
+    stream joins add time.  All compute is in the library's kernels."""
+
+    def __init__(self, topk=2048, overlap=False):
+        self.topk = int(topk)
+        self.overlap = bool(overlap)
+        self._side = None
+
+    def run(self, layers, *, m=4, q_pos0=0, kv_len=None, causal=True, scale=None):
+        """layers: sequence of ((q_I, k_I, w_I), (q, k, v)) per layer: the
+        indexer's inputs and the attention's.  Returns the attention outputs,
+        fp32 [B, S_q, H, Dv] per layer."""
+        torch = _torch()
+        kw = dict(m=m, q_pos0=q_pos0, kv_len=kv_len, causal=causal)
+        main = torch.cuda.current_stream()
+        if self.overlap and self._side is None:
+            self._side = torch.cuda.Stream()              # created once, default priority
+        sel = _topk_any(*layers[0][0], self.topk, **kw)
+        outs = []
+        for li, (ind, att) in enumerate(layers):
+            nxt = None
+            if 1 <= li < len(layers) - 1:                  # its result serves layer li+1
+                if self.overlap:
+                    self._side.wait_stream(main)
+                    with torch.cuda.stream(self._side):
+                        nxt = _topk_any(*ind, self.topk, **kw)
+                else:
+                    nxt = _topk_any(*ind, self.topk, **kw)
+            outs.append(sparse_attention(*att, sel, scale=scale))
+            if nxt is not None:
+                if self.overlap:
+                    main.wait_stream(self._side)
+                    nxt.record_stream(main)
+                sel = nxt
+        return outs
