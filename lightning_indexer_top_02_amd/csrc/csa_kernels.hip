@@ -997,17 +997,19 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_batch_kernel(De
 // outside [0, T) are skipped.  H = 64 heads, Dk = Dv = 128, bf16 inputs,
 // fp32 accumulation and output.
 //
-// attn_chunk_kernel: grid (nsplit, rows), 4 waves.  A workgroup takes the
-// row's 128-entry chunks split, split + nsplit, ... with an online softmax.
-// Per chunk: wave w gathers the key rows of entries 32w..32w+31 straight into
-// MFMA B operands (16 B per lane) and forms the 64 x 32 logits with the
-// query as the A operand (registers, loaded once); the chunk's per-head max
-// and the running max come through LDS; p = exp(z - m) goes to LDS as bf16 in
-// the MFMA A layout, the chunk's value rows go to LDS transposed (dv-major),
-// and wave w then accumulates output columns 32w..32w+31 of all 64 heads with
-// P.V MFMAs after rescaling them by exp(m_old - m_new).  Both LDS tiles are
-// XOR-swizzled in 16-byte pieces (piece ^ row % 16) so that the 16-byte
-// operand reads of 32 rows at the same piece spread over the banks.
+// attn_chunk_kernel: grid (nsplit, rows), 8 waves.  A workgroup takes the
+// row's AT_CHUNK-entry (256) chunks split, split + nsplit, ... with an online
+// softmax.  Per chunk: wave w gathers the key rows of entries 32w..32w+31
+// straight into MFMA B operands (16 B per lane), while every thread gathers
+// its share of the chunk's value rows, all in flight together; wave w forms
+// the 64 x 32 logits of its entries with the query slices (LDS, A operand);
+// the chunk's per-head max and the running max come through LDS; p =
+// exp(z - m) goes to LDS as bf16 in the MFMA A layout, the value rows go to
+// LDS transposed (dv-major), and wave w then accumulates head tile w % 2 for
+// output columns 32 * (w / 2) .. + 31 with P.V MFMAs after rescaling them by
+// exp(m_old - m_new).  Both LDS tiles are XOR-swizzled in 16-byte pieces
+// (piece ^ row % 16) so that the 16-byte operand reads of 32 rows at the same
+// piece spread over the banks.
 // attn_combine_kernel merges the nsplit partial results of a row.
 
 // Lane exchanges inside 16-lane rows through DPP (no LDS round trip):
