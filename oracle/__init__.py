@@ -11,3 +11,6 @@ from .csa_oracle import (  # noqa: F401
 )
 from .csa_attention_oracle import attention_row, oracle_attention  # noqa: F401
 from .csa_union_oracle import oracle_union, oracle_multilayer  # noqa: F401
+from .csa_projection_oracle import (  # noqa: F401
+    project, project_abs, oracle_query, oracle_head_weights, oracle_compress_keys,
+)
