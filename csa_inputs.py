@@ -158,3 +158,18 @@ def sample_rows(S_q: int, n: int, seed: int, must=()):
             break
         rows.add(int(r))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def make_projection(M, N, K, seed=0, kind="gauss"):
+    """Operands of a projection y = x . w^T as bf16 bit patterns: x [M, K] and
+    w [N, K].  kind "gauss": x ~ N(0,1), w ~ N(0,1)/sqrt(K) (unit-scale
+    outputs), rounded to bf16; kind "int": integers uniform in {-1, 0, 1}
+    (every sum exact, every output a bf16-representable integer for K <= 256)."""
+    rng = np.random.default_rng(seed)
+    if kind == "int":
+        x = rng.integers(-1, 2, size=(M, K)).astype(np.float32)
+        w = rng.integers(-1, 2, size=(N, K)).astype(np.float32)
+    else:
+        x = rng.standard_normal((M, K), dtype=np.float32)
+        w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(w)

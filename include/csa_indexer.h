@@ -203,6 +203,27 @@ csa_status csa_index_threshold_select_layers(const csa_problem* const* probs, in
                                              int32_t* const* out_count, float* const* out_score, void* ws,
                                              size_t ws_bytes, void* hip_stream);
 
+/* Dense projection y[M][N] = x[M][K] . w[N][K]^T with bf16 operands and
+ * fp32 accumulation: the producers of the indexer's inputs.  The FlashMemory
+ * review gives the Memory Indexer's query encoder a low-rank projection of
+ * dimension r = 2048; StreamIndex (abstract) scores keys compressed by a ratio
+ * m.  With x and w as below this computes, in the layouts the indexer entry
+ * points read (row-major, no conversion pass):
+ *   query        x = latents c [B*S][r],       w = W_q [H*D][r]   -> q [B,S,H,D] (bf16)
+ *   head weights x = hidden states [B*S][d],   w = W_w [H][d]     -> w [B,S,H]   (fp32)
+ *   compressed   x = token vectors [B*S/m][m*d_z] (the m tokens of a group
+ *   keys           side by side), w = W_k [D][m*d_z]              -> k [B,T,D]   (bf16)
+ * x: DEVICE bf16 [M][K], w: DEVICE bf16 [N][K], both row-major and 16-byte
+ * aligned; y: DEVICE [M][N] row-major, bf16 (round to nearest even) when
+ * out_dtype = CSA_BF16, fp32 when CSA_F32.  Caller owns all buffers; nothing
+ * is allocated; asynchronous on hip_stream.
+ * Errors: CSA_ERR_INVALID (NULL pointers with M > 0, M < 0, N or K < 1, bad
+ * out_dtype, misalignment); CSA_ERR_UNSUPPORTED (K not a multiple of 64,
+ * N > CSA_MAX_PROJECT_N, M above 2^31 - 256).  M = 0 is a no-op. */
+#define CSA_MAX_PROJECT_N (1 << 20)
+csa_status csa_project(const void* x, const void* w, int64_t M, int32_t N, int32_t K, int32_t out_dtype, void* y,
+                       void* hip_stream);
+
 /* Union of several selections per row (multi-layer selection: the
  * FlashMemory-DeepSeek-V4 review, "What carries the argument", places its
  * Memory Indexer on three layers and combines their keep decisions with a

@@ -69,6 +69,7 @@ _SIGS = {
     "csa_sparse_attention": (_i32, [_PA, _vp, _i32, _f32, _vp, _vp, _sz, _vp]),
     "csa_union_rows": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, ctypes.c_int64, _i32, _i32, _vp,
                               _vp, _vp]),
+    "csa_project": (_i32, [_vp, _vp, ctypes.c_int64, _i32, _i32, _i32, _vp, _vp]),
     "csa_status_str": (ctypes.c_char_p, [_i32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_version": (ctypes.c_int, []),
@@ -485,3 +486,47 @@ class MultiLayerIndexer:
                     nxt.record_stream(main)
                 sel = nxt
         return outs
+
+
+def project(x, w, *, out_dtype=None, out=None):
+    """y [..., N] = x [..., K] . w [N, K]^T (bf16 operands, fp32 accumulation);
+    bf16 output unless out_dtype=torch.float32.  K must be a multiple of 64."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    for name, t in (("x", x), ("w", w)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if w.dim() != 2 or x.shape[-1] != w.shape[1]:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)} w {tuple(w.shape)}")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    N, K = int(w.shape[0]), int(w.shape[1])
+    M = x.numel() // K if K else 0
+    y = out if out is not None else torch.empty(tuple(x.shape[:-1]) + (N,), dtype=out_dtype, device=x.device)
+    code = CSA_F32 if out_dtype == torch.float32 else CSA_BF16
+    _check(load_library().csa_project(_ptr(x), _ptr(w), int(M), N, K, code, _ptr(y), _stream_handle()))
+    return y
+
+
+def query_projection(c, wq, H=64):
+    """Indexer queries q [B, S, H, D] (bf16, head-major) from the low-rank
+    latents c [B, S, r] and W_q [H*D, r]."""
+    B, S = c.shape[0], c.shape[1]
+    return project(c, wq).view(B, S, H, wq.shape[0] // H)
+
+
+def head_weight_projection(x, ww):
+    """Indexer head weights w [B, S, H] (fp32) from hidden states x [B, S, d]
+    and W_w [H, d]."""
+    return project(x, ww, out_dtype=_torch().float32)
+
+
+def compress_keys(z, wk, m=4):
+    """Compressed keys k [B, S/m, D] (bf16): key s is W_k [D, m*d_z] applied to
+    the m token vectors z[b, m*s .. m*s+m-1] side by side (z [B, S, d_z])."""
+    B, S, dz = z.shape
+    if S % m:
+        raise ValueError("S must be a multiple of m")
+    return project(z.view(B, S // m, m * dz), wk)

@@ -422,6 +422,29 @@ csa_status csa_index_threshold_select_layers(const csa_problem* const* probs, in
   }
 }
 
+csa_status csa_project(const void* x, const void* w, int64_t M, int32_t N, int32_t K, int32_t out_dtype, void* y,
+                       void* hip_stream) {
+  try {
+    if (M < 0) return fail(CSA_ERR_INVALID, "M=%lld must be >= 0", (long long)M);
+    if (N < 1 || K < 1) return fail(CSA_ERR_INVALID, "N=%d and K=%d must be >= 1", N, K);
+    if (out_dtype != CSA_BF16 && out_dtype != CSA_F32) return fail(CSA_ERR_INVALID, "out_dtype must be CSA_BF16 or CSA_F32");
+    if (K % csa::PJ_BK) return fail(CSA_ERR_UNSUPPORTED, "K=%d must be a multiple of %d", K, csa::PJ_BK);
+    if (N > CSA_MAX_PROJECT_N) return fail(CSA_ERR_UNSUPPORTED, "N=%d above %d", N, CSA_MAX_PROJECT_N);
+    if (M > csa::project_rows_limit())
+      return fail(CSA_ERR_UNSUPPORTED, "M=%lld above %lld rows per call", (long long)M, csa::project_rows_limit());
+    if (M == 0) return ok();
+    if (!x || !w || !y) return fail(CSA_ERR_INVALID, "x, w and y must not be NULL");
+    if ((uintptr_t)x % 16 || (uintptr_t)w % 16) return fail(CSA_ERR_INVALID, "x and w must be 16-byte aligned");
+    if ((uintptr_t)y % (out_dtype == CSA_F32 ? 4 : 2)) return fail(CSA_ERR_INVALID, "y is misaligned");
+    csa::ProjArgs a{x, w, y, (long long)M, N, K, out_dtype == CSA_F32 ? 1 : 0};
+    const hipError_t e = csa::launch_project(a, N >= 256 ? 0 : 1, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "projection launch failed: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
 csa_status csa_index_topk_interleaved(const csa_problem* prob, int32_t P, int32_t k_local, uint32_t flags,
                                       int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
                                       void* hip_stream) {

@@ -98,6 +98,20 @@ constexpr int UN_MAX_LISTS = 8;
 constexpr int UN_MAX_T = 1 << 20;      // keys covered by the LDS bitmap (128 KiB)
 constexpr int UN_THREADS = 1024;
 
+// Dense projection y[M][N] = x[M][K] . w[N][K]^T, bf16 operands, fp32
+// accumulation, bf16 or fp32 output (the producers of the indexer's inputs).
+constexpr int PJ_BK = 64;              // K per pipeline step (K must be a multiple)
+struct ProjArgs {
+  const void* x;                       // bf16 [M][K]
+  const void* w;                       // bf16 [N][K]
+  void* y;                             // [M][N], bf16 or fp32
+  long long M;
+  int N, K;
+  int out_f32;
+};
+hipError_t launch_project(const ProjArgs& a, int variant, hipStream_t st);
+long long project_rows_limit();
+
 struct UnionArgs {
   const int32_t* list[UN_MAX_LISTS];   // list i: [rows][width[i]]
   int width[UN_MAX_LISTS];

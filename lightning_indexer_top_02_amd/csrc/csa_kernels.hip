@@ -1283,6 +1283,112 @@ __global__ __launch_bounds__(UN_THREADS) void union_rows_kernel(UnionArgs a) {
   if (tid == 0 && a.out_count) a.out_count[row] = total;
 }
 
+// ============================================================ projections
+//
+// The producers of the indexer's inputs are linear maps over bf16 operands:
+// the query's low-rank up-projection (r = 2048 -> H*D), the head weights, and
+// the m:1 key compression (the m token vectors of a group side by side).  All
+// are y = x . w^T with x [M][K], w [N][K] row-major, on MFMA with fp32
+// accumulation; the output goes straight to the layout the indexer reads (q
+// head-major [.., H, D] bf16, w fp32), so no conversion pass follows.
+//
+// A workgroup computes a BM x BN tile of y over K in steps of PJ_BK = 64:
+// the x and w tiles (16-byte pieces, 8 per 64-wide row) are loaded into
+// registers one step ahead and stored to the LDS buffer the MFMAs are not
+// reading (two buffers, one barrier per step).  LDS rows are 128 bytes; piece
+// p of row r sits in slot p ^ ((r >> 1) & 7), so the operand reads (32 rows at
+// one piece) cover all 16 16-byte bank groups of each 256-byte window.  Wave
+// (wm, wn) owns a (32*TM) x (32*TN) sub-tile; for each 16-deep slice it reads
+// TM A and TN B operands (lane: row l & 31, k half l >> 5) and issues TM*TN
+// v_mfma_f32_32x32x16_bf16.  Rows past M and columns past N load a clamped
+// (valid) row and are not stored.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * WAVE, 512 / (WGM * WGN * WAVE)) void project_kernel(ProjArgs a) {
+  constexpr int NT = WGM * WGN * WAVE;
+  constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;
+  constexpr int AP = BM * 8 / NT, BP = BN * 8 / NT;    // 16-byte pieces per thread and step
+  static_assert(AP * NT == BM * 8 && BP * NT == BN * 8 && TM >= 1 && TN >= 1, "tile shape");
+  __shared__ bf16x8 As[2][BM * 8];
+  __shared__ bf16x8 Bs[2][BN * 8];
+  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  const int wm = wv / WGN, wn = wv % WGN;
+  const long long m0 = (long long)blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+  const bf16x8* X = (const bf16x8*)a.x;
+  const bf16x8* W = (const bf16x8*)a.w;
+  const long long kp = a.K / 8;                        // pieces per row
+  const int nk = a.K / PJ_BK;
+  auto slot = [](int r, int p) { return r * 8 + (p ^ ((r >> 1) & 7)); };
+  bf16x8 ra[AP], rb[BP];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+      const int q = tid + NT * i, r = q >> 3, p = q & 7;
+      const long long gr = m0 + r < a.M ? m0 + r : a.M - 1;
+      ra[i] = X[gr * kp + kt * 8 + p];
+    }
+#pragma unroll
+    for (int i = 0; i < BP; ++i) {
+      const int q = tid + NT * i, r = q >> 3, p = q & 7;
+      const long long gn = n0 + r < a.N ? n0 + r : a.N - 1;
+      rb[i] = W[gn * kp + kt * 8 + p];
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+      const int q = tid + NT * i;
+      As[buf][slot(q >> 3, q & 7)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BP; ++i) {
+      const int q = tid + NT * i;
+      Bs[buf][slot(q >> 3, q & 7)] = rb[i];
+    }
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < PJ_BK / 16; ++kk) {
+      const int p = 2 * kk + (l >> 5);
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = As[cur][slot(wm * TM * 32 + i * 32 + (l & 31), p)];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = Bs[cur][slot(wn * TN * 32 + j * 32 + (l & 31), p)];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = n0 + wn * TN * 32 + j * 32 + (l & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const long long r = m0 + wm * TM * 32 + i * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+        if (r < a.M && c < a.N) {
+          if (a.out_f32) ((float*)a.y)[r * a.N + c] = acc[i][j][e];
+          else ((__bf16*)a.y)[r * a.N + c] = (__bf16)acc[i][j][e];
+        }
+      }
+    }
+}
+
 // ============================================================ row sort
 //
 // Sorts each row of `len` (index, score) pairs by (score desc, index asc);
@@ -1471,6 +1577,22 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_union(const UnionArgs& a, long long rows, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   union_rows_kernel<<<(unsigned)rows, UN_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// variant 0: 256 x 256 tiles, 8 waves of 128 x 64; variant 1: 128 x 128 tiles,
+// 4 waves of 64 x 64 (for outputs narrower than 256 columns).
+long long project_rows_limit() { return (1ll << 32) / 512 * 256 - 256; }
+
+hipError_t launch_project(const ProjArgs& a, int variant, hipStream_t st) {
+  if (a.M <= 0) return hipSuccess;
+  if (variant == 0) {
+    const dim3 grid((unsigned)((a.M + 255) / 256), (unsigned)((a.N + 255) / 256));
+    project_kernel<256, 256, 2, 4><<<grid, 512, 0, st>>>(a);
+  } else {
+    const dim3 grid((unsigned)((a.M + 127) / 128), (unsigned)((a.N + 127) / 128));
+    project_kernel<128, 128, 2, 2><<<grid, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

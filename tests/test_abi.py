@@ -245,3 +245,20 @@ def test_threshold_layers_argument_errors(lib):
     # the workspace is the per-layer threshold workspace times the layer count
     n1 = L.workspace_size(L.OP_THRESHOLD, dec(), 64, 1, 0)
     assert call([dec(), dec(), dec()], ws_bytes=3 * n1 - 1) == Bd.CSA_ERR_WORKSPACE
+
+
+def test_project_argument_errors(lib):
+    def call(M=300, N=200, K=128, dt=Bd.CSA_BF16, x=0x1000, w=0x2000, y=0x3000):
+        return lib.csa_project(x, w, M, N, K, dt, y, None)
+    assert call(M=-1) == Bd.CSA_ERR_INVALID
+    assert call(N=0) == Bd.CSA_ERR_INVALID
+    assert call(K=0) == Bd.CSA_ERR_INVALID
+    assert call(dt=7) == Bd.CSA_ERR_INVALID
+    assert call(K=100) == Bd.CSA_ERR_UNSUPPORTED                    # K must be a multiple of 64
+    assert call(N=(1 << 20) + 1) == Bd.CSA_ERR_UNSUPPORTED
+    assert call(M=1 << 31) == Bd.CSA_ERR_UNSUPPORTED
+    assert call(x=None) == Bd.CSA_ERR_INVALID
+    assert call(y=None) == Bd.CSA_ERR_INVALID
+    assert call(x=0x1008) == Bd.CSA_ERR_INVALID                     # 16-byte alignment
+    assert call(dt=Bd.CSA_F32, y=0x3002) == Bd.CSA_ERR_INVALID
+    assert call(M=0, x=None, w=None, y=None) == Bd.CSA_OK           # nothing to do

@@ -2,10 +2,11 @@
 
 Tolerance, from the arithmetic: logits and sums are fp32 over exact bf16
 products (relative error ~1e-6); the softmax weights are rounded to bf16
-(relative error <= 2^-9 each) and the normaliser sums the rounded weights, so
-the output is an exact convex combination whose weights are off by at most
-2 * 2^-9 relative.  Hence, per output element,
-    |o_gpu - o_ref| <= 2^-8 * max_e |v[idx_e, d]| + 1e-5,
+(8 significant bits: relative error <= 2^-8 each) and the normaliser sums the
+rounded weights, so the output is an exact convex combination whose weights
+are off by at most 2 * 2^-8 relative, i.e. their absolute errors sum to at
+most 2^-7.  Hence, per output element,
+    |o_gpu - o_ref| <= 2^-7 * max_e |v[idx_e, d]| + 1e-5,
 with max_e over the row's valid entries.  Cases whose weights are exactly
 representable (one dominant key, equal logits) are checked to 1e-5.
 """
@@ -48,7 +49,7 @@ def _check(p, o, rows=None):
             sel = p["idx"][b, t]
             sel = sel[(sel >= 0) & (sel < T)]
             vmax = np.abs(vv[b, sel]).max(axis=0) if len(sel) else np.zeros(p["Dv"])
-            tol = 2.0 ** -8 * vmax[None, :] + 1e-5
+            tol = 2.0 ** -7 * vmax[None, :] + 1e-5
             err = np.abs(o[b, t] - ref[b, t])
             assert (err <= tol).all(), f"row ({b},{t}): max err {err.max():.3e} over tolerance"
             worst = max(worst, float((err / tol).max()))

@@ -3,7 +3,7 @@ layer l >= 1 attends over layer l-1's top-k, layer 0 over its own; the
 overlapped schedule (indexer on a second stream) gives bit-identical outputs
 to the same schedule on one stream, and each layer matches the CPU oracle's
 attention over the oracle's selection (attention tolerance as in the sparse
-attention tests: 2^-8 * max|v| + 1e-5 per element)."""
+attention tests: 2^-7 * max|v| + 1e-5 per element)."""
 import numpy as np
 import pytest
 
@@ -60,5 +60,5 @@ def test_mli_schedule_matches_oracle(S_q):
         for b in range(B):
             for t in range(S_q):
                 s = sel[b, t][sel[b, t] >= 0]
-                tol = 2.0 ** -8 * np.abs(vv[b, s]).max(axis=0)[None, :] + 1e-5
+                tol = 2.0 ** -7 * np.abs(vv[b, s]).max(axis=0)[None, :] + 1e-5
                 assert (np.abs(outs[True][li][b, t] - ref[b, t]) <= tol).all(), f"layer {li} row ({b},{t})"

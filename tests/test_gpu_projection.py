@@ -1,0 +1,150 @@
+"""GPU parity of csa_project and the producers of the indexer's inputs built
+on it (query projection, head weights, m:1 key compression).
+
+Tolerance, from the arithmetic: bf16 x bf16 products are exact in fp32; the
+fp32 accumulation over K terms is off by at most about K * 2^-24 * S, with
+S = sum_k |x_k| |w_k| (the oracle's project_abs); a bf16 output (8
+significant bits, round to nearest even) adds at most 2^-8 relative.  The
+tests allow
+    |y_gpu - y_ref| <= 2^-8 |y_ref| + K * 2^-22 * S      (bf16 output)
+    |y_gpu - y_ref| <= K * 2^-23 * S                     (fp32 output)
+Integer operands in {-1, 0, 1} with K <= 256 make every sum and every output
+exact, and those cases are compared bit for bit; integer sums above 256 pin
+the output rounding (nearest, ties to even) bit for bit.
+"""
+import numpy as np
+import pytest
+
+import csa_inputs
+import gpu_common
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import lightning_indexer_top_02_amd as L  # noqa: E402
+
+
+def _say(msg):
+    print(f"[csa-test] {msg}", flush=True)
+
+
+def _bf(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _host(y):
+    if y.dtype == torch.bfloat16:
+        return oracle.decode_bf16(y.view(torch.int16).cpu().numpy().view(np.uint16))
+    return y.double().cpu().numpy()
+
+
+def _check(got, xb, wb, K, bf16_out):
+    ref = oracle.project(xb, wb)
+    tol = K * 2.0 ** -23 * oracle.project_abs(xb, wb)
+    if bf16_out:
+        tol = 2 * tol + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), f"max err/tol {(err / np.maximum(tol, 1e-30)).max():.3f}"
+    return float((err / np.maximum(tol, 1e-30)).max())
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 192),     # 128-wide tiles, ragged rows and columns
+                                   (517, 640, 128),     # 256-wide tiles, ragged rows and columns
+                                   (1, 256, 64)])       # one row, one k step
+def test_project_exact_integers(M, N, K):
+    xb, wb = csa_inputs.make_projection(M, N, K, seed=M + N, kind="int")
+    ref = oracle.project(xb, wb)
+    _say(f"project exact M={M} N={N} K={K}")
+    for dt in (torch.bfloat16, torch.float32):
+        y = L.project(_bf(xb), _bf(wb), out_dtype=dt)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host(y), ref), f"dtype {dt}"
+
+
+def test_project_output_rounding_is_nearest_even():
+    """Operands in {0, 1} with K = 448: every fp32 sum is an exact integer up
+    to 448, and the bf16 output must be that integer rounded to nearest, ties
+    to even (257 -> 256, 259 -> 260, 261 -> 260, ...)."""
+    M, N, K = 300, 260, 448
+    rng = np.random.default_rng(99)
+    x = (rng.random((M, K)) < 0.8).astype(np.float32)
+    w = (rng.random((N, K)) < 0.9).astype(np.float32)
+    xb, wb = csa_inputs.f32_to_bf16_bits(x), csa_inputs.f32_to_bf16_bits(w)
+    exact = oracle.project(xb, wb)
+    assert (exact > 256).mean() > 0.5                              # most outputs need rounding
+    want = oracle.decode_bf16(csa_inputs.f32_to_bf16_bits(exact.astype(np.float32)))
+    y = L.project(_bf(xb), _bf(wb))
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(y), want)
+
+
+@pytest.mark.parametrize("M,N,K", [(777, 384, 512), (129, 100, 2048)])
+def test_project_gaussian_tolerance(M, N, K):
+    xb, wb = csa_inputs.make_projection(M, N, K, seed=7 * M + K)
+    _say(f"project gaussian M={M} N={N} K={K}")
+    for dt in (torch.bfloat16, torch.float32):
+        y = L.project(_bf(xb), _bf(wb), out_dtype=dt)
+        torch.cuda.synchronize()
+        _say(f"  {dt}: worst err / tolerance = {_check(_host(y), xb, wb, K, dt == torch.bfloat16):.3f}")
+
+
+def test_project_empty():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    assert L.project(x, w).shape == (0, 64)
+
+
+def test_query_projection_full_size_sampled_rows():
+    """S=16384 latents of width r=2048 -> q [1, 16384, 64, 128]; sampled rows
+    (tile edges, the last row, seeded picks) against the oracle."""
+    S, r, H, D = 16384, 2048, 64, 128
+    cb, wqb = csa_inputs.make_projection(S, H * D, r, seed=2048)
+    _say("query projection S=16384 r=2048 -> 64 x 128")
+    q = L.query_projection(_bf(cb).view(1, S, r), _bf(wqb), H=H)
+    torch.cuda.synchronize()
+    assert tuple(q.shape) == (1, S, H, D)
+    rows = sorted(set([0, 1, 255, 256, 257, 8191, S - 1] + list(np.random.default_rng(3).integers(0, S, 9))))
+    got = _host(q[0, rows].contiguous())
+    ref = oracle.oracle_query(cb[rows][None], wqb, H, D)[0]
+    tol = r * 2.0 ** -22 * oracle.project_abs(cb[rows], wqb).reshape(len(rows), H, D) + 2.0 ** -8 * np.abs(ref)
+    assert (np.abs(got - ref) <= tol).all()
+
+
+def test_head_weights_and_key_compression():
+    B, S, d, H = 2, 300, 256, 64
+    xb, wwb = csa_inputs.make_projection(B * S, H, d, seed=5)
+    w = L.head_weight_projection(_bf(xb).view(B, S, d), _bf(wwb))
+    torch.cuda.synchronize()
+    assert w.dtype == torch.float32 and tuple(w.shape) == (B, S, H)
+    _check(_host(w).reshape(B * S, H), xb, wwb, d, False)
+    m, dz, D = 4, 128, 128
+    zb, wkb = csa_inputs.make_projection(B * 128, D, m * dz, seed=6)   # 128 groups of 4 tokens of width 128
+    zb = zb.reshape(B, 512, dz)
+    k = L.compress_keys(_bf(zb), _bf(wkb), m=m)
+    torch.cuda.synchronize()
+    assert tuple(k.shape) == (B, 128, D)
+    ref = oracle.oracle_compress_keys(zb, wkb, m)
+    tol = m * dz * 2.0 ** -22 * oracle.project_abs(zb.reshape(B, 128, m * dz), wkb) + 2.0 ** -8 * np.abs(ref)
+    assert (np.abs(_host(k) - ref) <= tol).all()
+
+
+def test_produced_inputs_feed_the_indexer():
+    """q, w and compressed k made on the GPU go straight into the top-k entry
+    point; its selection matches the oracle's top-k over the same tensors
+    (bf16 inputs: the indexer's set tolerance rule)."""
+    B, S, r, d, H, D, m, topk = 1, 256, 256, 128, 64, 128, 4, 16
+    cb, wqb = csa_inputs.make_projection(S, H * D, r, seed=11)
+    xb, wwb = csa_inputs.make_projection(S, H, d, seed=12)
+    zb, wkb = csa_inputs.make_projection(S, D, d, seed=13)
+    wkb = csa_inputs.make_projection(1, D, m * d, seed=14)[1]
+    q = L.query_projection(_bf(cb).view(B, S, r), _bf(wqb), H=H)
+    w = L.head_weight_projection(_bf(xb).view(B, S, d), _bf(wwb))
+    k = L.compress_keys(_bf(zb).view(B, S, d), _bf(wkb), m=m)
+    idx = L.index_topk_prefill(q, k, w, topk, m=m, q_pos0=0)
+    torch.cuda.synchronize()
+    p = dict(dtype="bf16", B=B, S_q=S, T=S // m, H=H, D=D, m=m, q_pos0=0, topk=topk,
+             q=q.view(torch.int16).cpu().numpy().view(np.uint16), k=k.view(torch.int16).cpu().numpy().view(np.uint16),
+             w=w.cpu().numpy(), kv_len=None, causal=True)
+    stats = gpu_common.check_tolerance(p, list(range(S)), idx.cpu().numpy(), None, topk)
+    _say(f"  {stats['rows']} rows, {stats['swaps']} boundary swaps")
