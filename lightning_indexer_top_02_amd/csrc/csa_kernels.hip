@@ -1292,71 +1292,65 @@ __global__ __launch_bounds__(UN_THREADS) void union_rows_kernel(UnionArgs a) {
 // accumulation; the output goes straight to the layout the indexer reads (q
 // head-major [.., H, D] bf16, w fp32), so no conversion pass follows.
 //
-// A workgroup computes a BM x BN tile of y over K in steps of PJ_BK = 64:
-// the x and w tiles (16-byte pieces, 8 per 64-wide row) are loaded into
-// registers one step ahead and stored to the LDS buffer the MFMAs are not
-// reading (two buffers, one barrier per step).  LDS rows are 128 bytes; piece
-// p of row r sits in slot p ^ ((r >> 1) & 7), so the operand reads (32 rows at
-// one piece) cover all 16 16-byte bank groups of each 256-byte window.  Wave
+// A workgroup computes a BM x BN tile of y over K in steps of PJ_BK = 64.
+// The x and w tiles go straight from memory into LDS (global_load_lds_dwordx4:
+// no staging registers, no LDS store instructions), into one of two buffers:
+// the next step's tiles are requested before this step's MFMAs and waited
+// for (vmcnt) before the step's barrier.  LDS rows are 128 bytes (8 pieces of
+// 16 bytes); piece p of row r sits in slot p ^ ((r >> 1) & 7), so that the
+// operand reads (32 rows at one piece) cover all 16 16-byte bank groups of
+// each 256-byte window.  A wave fills 1-KB blocks of 8 rows, lane i writing
+// row i / 8, slot i % 8, so it fetches the piece that slot holds.  Wave
 // (wm, wn) owns a (32*TM) x (32*TN) sub-tile; for each 16-deep slice it reads
 // TM A and TN B operands (lane: row l & 31, k half l >> 5) and issues TM*TN
 // v_mfma_f32_32x32x16_bf16.  Rows past M and columns past N load a clamped
 // (valid) row and are not stored.
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * WAVE, 512 / (WGM * WGN * WAVE)) void project_kernel(ProjArgs a) {
-  constexpr int NT = WGM * WGN * WAVE;
+  constexpr int NT = WGM * WGN * WAVE, NW = NT / WAVE;
   constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;
-  constexpr int AP = BM * 8 / NT, BP = BN * 8 / NT;    // 16-byte pieces per thread and step
-  static_assert(AP * NT == BM * 8 && BP * NT == BN * 8 && TM >= 1 && TN >= 1, "tile shape");
-  __shared__ bf16x8 As[2][BM * 8];
-  __shared__ bf16x8 Bs[2][BN * 8];
+  constexpr int AC = BM / 8 / NW, BC = BN / 8 / NW;    // 1-KB blocks per wave and step
+  static_assert(AC * NW * 8 == BM && BC * NW * 8 == BN && TM >= 1 && TN >= 1, "tile shape");
+  __shared__ __attribute__((aligned(1024))) bf16x8 As[2][BM * 8];
+  __shared__ __attribute__((aligned(1024))) bf16x8 Bs[2][BN * 8];
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int wm = wv / WGN, wn = wv % WGN;
   const long long m0 = (long long)blockIdx.x * BM;
   const int n0 = blockIdx.y * BN;
-  const bf16x8* X = (const bf16x8*)a.x;
-  const bf16x8* W = (const bf16x8*)a.w;
-  const long long kp = a.K / 8;                        // pieces per row
+  const long long kp = a.K / 8;
   const int nk = a.K / PJ_BK;
   auto slot = [](int r, int p) { return r * 8 + (p ^ ((r >> 1) & 7)); };
-  bf16x8 ra[AP], rb[BP];
-  auto gload = [&](int kt) {
+  const bf16x8* asrc[AC];
+  const bf16x8* bsrc[BC];
 #pragma unroll
-    for (int i = 0; i < AP; ++i) {
-      const int q = tid + NT * i, r = q >> 3, p = q & 7;
-      const long long gr = m0 + r < a.M ? m0 + r : a.M - 1;
-      ra[i] = X[gr * kp + kt * 8 + p];
-    }
+  for (int c = 0; c < AC; ++c) {
+    const int r = 8 * (wv + NW * c) + (l >> 3);
+    const long long gr = m0 + r < a.M ? m0 + r : a.M - 1;
+    asrc[c] = (const bf16x8*)a.x + gr * kp + ((l & 7) ^ ((r >> 1) & 7));
+  }
 #pragma unroll
-    for (int i = 0; i < BP; ++i) {
-      const int q = tid + NT * i, r = q >> 3, p = q & 7;
-      const long long gn = n0 + r < a.N ? n0 + r : a.N - 1;
-      rb[i] = W[gn * kp + kt * 8 + p];
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int c = 0; c < BC; ++c) {
+    const int r = 8 * (wv + NW * c) + (l >> 3);
+    const long long gn = n0 + r < a.N ? n0 + r : a.N - 1;
+    bsrc[c] = (const bf16x8*)a.w + gn * kp + ((l & 7) ^ ((r >> 1) & 7));
+  }
+  auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < AP; ++i) {
-      const int q = tid + NT * i;
-      As[buf][slot(q >> 3, q & 7)] = ra[i];
-    }
+    for (int c = 0; c < AC; ++c) dma16(asrc[c] + kt * 8, lds_addr(&As[buf][64 * (wv + NW * c)]));
 #pragma unroll
-    for (int i = 0; i < BP; ++i) {
-      const int q = tid + NT * i;
-      Bs[buf][slot(q >> 3, q & 7)] = rb[i];
-    }
+    for (int c = 0; c < BC; ++c) dma16(bsrc[c] + kt * 8, lds_addr(&Bs[buf][64 * (wv + NW * c)]));
   };
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-  gload(0);
-  sstore(0);
+  issue(0, 0);
+  wait_vmcnt<0>();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
 #pragma unroll
     for (int kk = 0; kk < PJ_BK / 16; ++kk) {
       const int p = 2 * kk + (l >> 5);
@@ -1370,7 +1364,7 @@ __global__ __launch_bounds__(WGM * WGN * WAVE, 512 / (WGM * WGN * WAVE)) void pr
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    wait_vmcnt<0>();
     __syncthreads();
   }
 #pragma unroll
