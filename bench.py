@@ -19,6 +19,8 @@ Also reported on the same JSON line:
                 at the decode shape, in GB/s of indexer keys against HBM peak,
                 and a three-layer stack with previous-layer reuse (indexer
                 top-k plus sparse attention per layer);
+  projection    the query projection that produces the prefill workload's q
+                (S=16384, r=2048 -> 64 x 128) in TFLOP/s against bf16 peak;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same rows.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50]
@@ -281,6 +283,42 @@ def _bench_mli(args, torch, L, R, ind_layers, p):
                          "(64 heads, d=128) for layers 0-2 over the previous layer's selection")
 
 
+def bench_projection(args, torch, L, csa_inputs, R):
+    """The query projection feeding the prefill workload: S=16384 low-rank
+    latents of width r=2048 -> q [16384, 64, 128] (bf16 operands, fp32
+    accumulation, bf16 out), through csa_project.  MFMA-bound: 2*S*r*H*D flops."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    S, r, H, D = 16384, 2048, 64, 128
+    cb, wqb = csa_inputs.make_projection(S, H * D, r, seed=1011)
+    c = torch.from_numpy(cb.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq = torch.from_numpy(wqb.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty((S, H * D), dtype=torch.bfloat16, device=dev)
+    lib = L.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cp, wp, yp = (ctypes.c_void_p(t.data_ptr()) for t in (c, wq, y))
+
+    def call(_):
+        st = lib.csa_project(cp, wp, S, H * D, r, L.CSA_BF16, yp, stream)
+        if st != 0:
+            raise RuntimeError(lib.csa_last_error().decode())
+
+    flops = 2.0 * S * r * H * D
+    steps = max(args.steps // 2, 20)
+    total_ms, avg_ms, med_ms, _ = _time_calls(torch, call, steps, min(args.warmup, 20))
+    ms = total_ms / steps
+    tf = flops / (ms * 1e-3) / 1e12
+    _log(f"query projection: {ms * 1e3:.1f} us per call, {tf:.0f} TFLOP/s")
+    tr = _traffic_record("project_kernel<256,256>")
+    del c, wq, y
+    torch.cuda.empty_cache()
+    return dict(value=round(tf, 1), unit="TFLOP/s", ms_per_call=round(ms, 5),
+                frac_bf16_peak=round(tf / R.PEAK_BF16_TFLOPS, 4), flops_per_call=flops, calls=steps,
+                launch_ms_avg=round(avg_ms, 5), launch_ms_median=round(med_ms, 5),
+                traffic=None if tr is None else tr["hbm_bytes_per_launch"],
+                workload="query projection S=16384, r=2048 -> H_I*d_I=8192, bf16 in/out, fp32 accumulate")
+
+
 def cpu_baseline(seconds, R):
     """Time the fp64 CPU oracle on the prefill workload: all rows when they fit
     the time budget (they do on a 16-core host: ~3 s), else a seeded sample of
@@ -334,6 +372,7 @@ def main():
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-multilayer", action="store_true")
     ap.add_argument("--no-mli", action="store_true", help="skip the previous-layer reuse timing")
+    ap.add_argument("--no-projection", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (reference for the HBM byte counters)")
@@ -372,6 +411,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, torch, L, csa_inputs, R)
     att = None if args.no_attention else bench_attention(args, torch, L, csa_inputs, R)
     mls = None if args.no_multilayer else bench_multilayer(args, torch, L, csa_inputs, R)
+    prj = None if args.no_projection else bench_projection(args, torch, L, csa_inputs, R)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, R)
 
     p = pf["p"]
@@ -415,6 +455,7 @@ def main():
         "decode": dec,
         "attention": att,
         "multilayer": mls,
+        "projection": prj,
         "peak_mem_bytes": pf["peak_mem"],
         "workspace_bytes": pf["ws"],
         "materialised_score_tensor_bytes": R.materialised_score_bytes(1, p["S_q"], p["H"], p["T"]),
