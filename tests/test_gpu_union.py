@@ -94,3 +94,33 @@ def test_batched_threshold_matches_per_layer(case):
         assert torch.equal(gc, rc)
         a, b = gi.cpu().numpy(), ri.cpu().numpy()
         assert (np.sort(a, axis=-1) == np.sort(b, axis=-1)).all()
+
+
+def test_batched_threshold_sorted_with_scores_eight_layers():
+    """The C entry point with all 8 layers, CSA_SORTED and score outputs: each
+    layer's indices, scores and order equal a separate sorted call's."""
+    import ctypes
+    from lightning_indexer_top_02_amd import _binding as Bd
+    probs = [_layer(s, S_q=4, T=700) for s in range(51, 59)]
+    layers = [_dev(p) for p in probs]
+    cap, n = 48, len(layers)
+    B, S_q = 2, 4
+    cps = [L.make_problem(q, k, w, m=4, q_pos0=probs[0]["q_pos0"]) for q, k, w in layers]
+    idx = [torch.empty((B, S_q, cap), dtype=torch.int32, device="cuda") for _ in range(n)]
+    cnt = [torch.empty((B, S_q), dtype=torch.int32, device="cuda") for _ in range(n)]
+    sco = [torch.empty((B, S_q, cap), dtype=torch.float32, device="cuda") for _ in range(n)]
+    nws = n * L.workspace_size(L.OP_THRESHOLD, cps[0], cap, 1, L.CSA_SORTED)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    PP = (ctypes.POINTER(Bd.CsaProblem) * n)(*[ctypes.pointer(p) for p in cps])
+    V = ctypes.c_void_p * n
+    _say("batched threshold selection: 8 layers, sorted, with scores")
+    st = L.load_library().csa_index_threshold_select_layers(
+        PP, n, 0.5, 0.0, cap, L.CSA_SORTED, V(*[t.data_ptr() for t in idx]), V(*[t.data_ptr() for t in cnt]),
+        V(*[t.data_ptr() for t in sco]), ctypes.c_void_p(ws.data_ptr()), nws,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, L.load_library().csa_last_error()
+    for li, (q, k, w) in enumerate(layers):
+        ri, rc, rs = L.index_threshold_select(q, k, w, cap, prob_threshold=0.5, m=4, q_pos0=probs[0]["q_pos0"],
+                                              sorted=True, return_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(cnt[li], rc) and torch.equal(idx[li], ri) and torch.equal(sco[li], rs), f"layer {li}"
