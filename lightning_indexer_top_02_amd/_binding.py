@@ -513,6 +513,8 @@ def project(x, w, *, out_dtype=None, out=None):
 def query_projection(c, wq, H=64):
     """Indexer queries q [B, S, H, D] (bf16, head-major) from the low-rank
     latents c [B, S, r] and W_q [H*D, r]."""
+    if c.dim() != 3 or wq.dim() != 2 or wq.shape[0] % H:
+        raise ValueError(f"expected c [B, S, r] and W_q [H*D, r] with H={H}: c {tuple(c.shape)} W_q {tuple(wq.shape)}")
     B, S = c.shape[0], c.shape[1]
     return project(c, wq).view(B, S, H, wq.shape[0] // H)
 
@@ -520,13 +522,19 @@ def query_projection(c, wq, H=64):
 def head_weight_projection(x, ww):
     """Indexer head weights w [B, S, H] (fp32) from hidden states x [B, S, d]
     and W_w [H, d]."""
+    if x.dim() != 3 or ww.dim() != 2:
+        raise ValueError(f"expected x [B, S, d] and W_w [H, d]: x {tuple(x.shape)} W_w {tuple(ww.shape)}")
     return project(x, ww, out_dtype=_torch().float32)
 
 
 def compress_keys(z, wk, m=4):
     """Compressed keys k [B, S/m, D] (bf16): key s is W_k [D, m*d_z] applied to
     the m token vectors z[b, m*s .. m*s+m-1] side by side (z [B, S, d_z])."""
+    if z.dim() != 3 or wk.dim() != 2:
+        raise ValueError(f"expected z [B, S, d_z] and W_k [D, m*d_z]: z {tuple(z.shape)} W_k {tuple(wk.shape)}")
     B, S, dz = z.shape
     if S % m:
         raise ValueError("S must be a multiple of m")
+    if not z.is_contiguous():
+        raise ValueError("z must be contiguous")
     return project(z.view(B, S // m, m * dz), wk)
