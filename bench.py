@@ -105,14 +105,14 @@ def _traffic_record(kernel):
     return None
 
 
-def bench_prefill(args, torch, L, csa_inputs, R):
+def bench_prefill(args, torch, L, csa_inputs, R, cfg=2):
     dev = torch.device("cuda:0")
-    p = csa_inputs.config(2)
+    p = csa_inputs.config(cfg)
     q, k, w = _to_dev(p, torch, dev)
     topk = p["topk"]
     prob = L.make_problem(q, k, w, m=p["m"], q_pos0=p["q_pos0"])
     lib = L.load_library()
-    out = torch.empty((1, p["S_q"], topk), dtype=torch.int32, device=dev)
+    out = torch.empty((p["B"], p["S_q"], topk), dtype=torch.int32, device=dev)
     nws = L.workspace_size(L.OP_PREFILL, prob, topk)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -373,6 +373,8 @@ def main():
     ap.add_argument("--no-multilayer", action="store_true")
     ap.add_argument("--no-mli", action="store_true", help="skip the previous-layer reuse timing")
     ap.add_argument("--no-projection", action="store_true")
+    ap.add_argument("--prefill-configs", default="",
+                    help="also time the prefill on these configs, e.g. 3,5 (S=65536; million-token tail)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (reference for the HBM byte counters)")
@@ -412,6 +414,21 @@ def main():
     att = None if args.no_attention else bench_attention(args, torch, L, csa_inputs, R)
     mls = None if args.no_multilayer else bench_multilayer(args, torch, L, csa_inputs, R)
     prj = None if args.no_projection else bench_projection(args, torch, L, csa_inputs, R)
+    other = {}
+    for cfg in [int(c) for c in args.prefill_configs.split(",") if c]:
+        torch.cuda.reset_peak_memory_stats()
+        save = args.steps
+        args.steps = max(10, args.steps // 10)
+        r = bench_prefill(args, torch, L, csa_inputs, R, cfg)
+        args.steps = save
+        tf = r["flops"] / (r["ms"] * 1e-3) / 1e12
+        _log(f"prefill config {cfg}: {r['ms']:.3f} ms per step, {tf:.1f} TFLOP/s, peak {r['peak_mem'] / 1e9:.2f} GB")
+        other[str(cfg)] = dict(workload=r["p"]["name"], ms_per_step=round(r["ms"], 4), value=round(tf, 1),
+                               unit="TFLOP/s", frac_bf16_peak=round(tf / R.PEAK_BF16_TFLOPS, 4),
+                               flops_per_step=r["flops"], steps=max(10, args.steps // 10),
+                               peak_mem_bytes=r["peak_mem"], workspace_bytes=r["ws"],
+                               materialised_score_tensor_bytes=R.materialised_score_bytes(
+                                   r["p"]["B"], r["p"]["q_pos0"] + r["p"]["S_q"], r["p"]["H"], r["p"]["T"]))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, R)
 
     p = pf["p"]
@@ -456,6 +473,7 @@ def main():
         "attention": att,
         "multilayer": mls,
         "projection": prj,
+        "prefill_other_configs": other or None,
         "peak_mem_bytes": pf["peak_mem"],
         "workspace_bytes": pf["ws"],
         "materialised_score_tensor_bytes": R.materialised_score_bytes(1, p["S_q"], p["H"], p["T"]),
