@@ -76,7 +76,7 @@ enum {
   CSA_OP_RECALL = 4
 };
 
-/* Limits of this build. */
+/* Limits of this library version. */
 #define CSA_MAX_TOPK 4096   /* topk, cap and k_local */
 #define CSA_MAX_HEADS 128
 #define CSA_MAX_DECODE_SQ 16
@@ -170,7 +170,7 @@ csa_status csa_set_recall(const int32_t* sel, int32_t n_sel, const int32_t* ref,
  * over the entries e of idx[b,t,0:n_sel] with 0 <= idx < T (others skipped;
  * an index listed twice counts twice); a row with no valid entry gives 0.
  * q [B,S_q,H,Dk], k [B,T,Dk], v [B,T,Dv] bf16; idx [B,S_q,n_sel] int32 (for
- * example out_idx of a top-k call); out [B,S_q,H,Dv] fp32.  This build:
+ * example out_idx of a top-k call); out [B,S_q,H,Dv] fp32.  Supported:
  * H = 64, Dk = Dv = 128 (CSA_ERR_UNSUPPORTED otherwise); n_sel >= 1; scale
  * finite.  Computed in fp32 from bf16 inputs with the softmax weights rounded
  * to bf16 for the weighted sum of value rows. */

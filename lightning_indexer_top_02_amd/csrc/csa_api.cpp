@@ -208,7 +208,7 @@ const char* csa_status_str(csa_status s) {
   switch (s) {
     case CSA_OK: return "CSA_OK";
     case CSA_ERR_INVALID: return "CSA_ERR_INVALID: invalid argument";
-    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape or parameter not supported by this build";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape or parameter not supported by this library version";
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace too small";
     case CSA_ERR_DEVICE: return "CSA_ERR_DEVICE: HIP runtime or launch failure";
   }
