@@ -7,8 +7,9 @@ here, so the two see bit-identical data.
 
 Workload shapes follow the V4-Flash indexer dimensions the StreamIndex paper
 (arXiv 2605.02568, abstract) measures on: H_I = 64 indexer heads over
-keys compressed by m = 4.  The paper gives no value distribution ("synthetic
-V4-shaped inputs at the indexer-step level"), so the recipe here is:
+keys compressed by m = 4.  The paper says only that its inputs are synthetic
+and shaped like V4's indexer step, with no value distribution, so the recipe
+here is:
 
 * bf16 configs: q, k ~ N(0,1)/sqrt(d_I) drawn in fp32 and rounded to bf16
   with round-to-nearest-even; w ~ N(0,1)/sqrt(H_I) kept in fp32.
