@@ -51,7 +51,9 @@ def _check(got, xb, wb, K, bf16_out):
 
 @pytest.mark.parametrize("M,N,K", [(300, 200, 192),     # 128-wide tiles, ragged rows and columns
                                    (517, 640, 128),     # 256-wide tiles, ragged rows and columns
-                                   (1, 256, 64)])       # one row, one k step
+                                   (1, 256, 64),        # one row, one k step
+                                   (1000, 1, 128),      # one output column
+                                   (129, 257, 256)])    # 256-wide tiles, one column past a tile
 def test_project_exact_integers(M, N, K):
     xb, wb = csa_inputs.make_projection(M, N, K, seed=M + N, kind="int")
     ref = oracle.project(xb, wb)
@@ -79,7 +81,7 @@ def test_project_output_rounding_is_nearest_even():
     assert np.array_equal(_host(y), want)
 
 
-@pytest.mark.parametrize("M,N,K", [(777, 384, 512), (129, 100, 2048)])
+@pytest.mark.parametrize("M,N,K", [(777, 384, 512), (129, 100, 2048), (64, 300, 8192)])
 def test_project_gaussian_tolerance(M, N, K):
     xb, wb = csa_inputs.make_projection(M, N, K, seed=7 * M + K)
     _say(f"project gaussian M={M} N={N} K={K}")
