@@ -54,6 +54,7 @@ struct DecodeArgs {
   float* scores;        // [B*S_q][T + DEC_PAD] fp32 workspace
   uint4* bounds;        // [B*S_q][nbw] per-wave selection bounds {order bits, count, max order bits, 0}
   int nbw;              // bounds per row: DEC_THREADS / WAVE per key chunk
+  int chunk;            // keys per scan workgroup: DEC_CHUNK or DEC_CHUNK_LONG
   int kk;
   int32_t* out_idx;
   float* out_score;
@@ -68,6 +69,7 @@ struct DecodeBatch {
 
 constexpr int DEC_THREADS = 256;
 constexpr int DEC_CHUNK = 1024;        // keys per decode-scan workgroup
+constexpr int DEC_CHUNK_LONG = 2048;   // ... for long rows with enough workgroups (DecodeArgs::chunk)
 constexpr int DEC_RING = 3;            // key-row buffers per wave in the decode scan
 constexpr int DEC_PAD = 64;            // floats after each score row (stores of keys past the end)
 constexpr int DEC_SEL_THREADS = 1024;

@@ -599,12 +599,13 @@ __device__ __forceinline__ int decode_visible(const DecodeArgs& a, int b, int i)
   return (int)v;
 }
 
+template <int CH>
 __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.y, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
-  const int start = blockIdx.x * DEC_CHUNK;
-  const int end = start + DEC_CHUNK < vis ? start + DEC_CHUNK : vis;
+  const int start = blockIdx.x * CH;
+  const int end = start + CH < vis ? start + CH : vis;
   if (start >= end) return;
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
@@ -623,9 +624,9 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) bf[kk] = src[2 * kk + (l >> 5)];
   };
-  static_assert(DEC_CHUNK % STRIDE == 0, "decode chunk must be whole steps");
+  static_assert(CH % STRIDE == 0, "decode chunk must be whole steps");
   static_assert(DEC_THREADS / WAVE * 2 == 8, "each wave copies two query slices");
-  constexpr int NSTEP = DEC_CHUNK / STRIDE;
+  constexpr int NSTEP = CH / STRIDE;
   const int base0 = start + STEP * wv;
   bf16x8 qa[2][2];
 #pragma unroll
@@ -684,7 +685,7 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
   {
     constexpr u64 LO = 0xFFFFFFFFull;                  // lanes 32-63 repeat lanes 0-31
     constexpr int WPC = DEC_THREADS / WAVE;            // waves per chunk
-    const int nfull = vis / DEC_CHUNK * WPC;           // waves with all DEC_CHUNK / WPC keys
+    const int nfull = vis / CH * WPC;                  // waves with all CH / WPC keys
     const int g = nfull > 0 ? (a.kk + nfull - 1) / nfull : 0x7FFFFFFF;
     uint32_t t1 = 0u, t2 = 0u, mn = ~0u;               // 0 is below every score's order bits
     int nv = 0;
@@ -714,11 +715,13 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs a) { decode_score_body(a); }
+template <int CH>
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_kernel(DecodeArgs a) { decode_score_body<CH>(a); }
 
 // Several problems of one shape in one launch (grid z = problem).
+template <int CH>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_batch_kernel(DecodeBatch bt) {
-  decode_score_body(bt.a[blockIdx.z]);
+  decode_score_body<CH>(bt.a[blockIdx.z]);
 }
 
 // decode_select: one workgroup per query row; exact top-kk of the row's
@@ -798,7 +801,7 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
     const int last = vis > 0 ? vis - 1 : 0;
     // the row's bounds first: loads complete in order, so reducing them does
     // not wait for the score loads behind them
-    const int nwr = (vis + DEC_CHUNK - 1) / DEC_CHUNK * (DEC_THREADS / WAVE);   // <= 128 here
+    const int nwr = (vis + a.chunk - 1) / a.chunk * (DEC_THREADS / WAVE);   // <= 128 here
     const uint4 bd = tid < nwr && vis > a.kk ? a.bounds[(size_t)row * a.nbw + tid] : make_uint4(~0u, 0u, 0u, 0u);
     float v[DEC_REG];
 #pragma unroll
@@ -1542,7 +1545,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, h
 
 hipError_t launch_decode_batch(const DecodeBatch& bt, int nsplit, hipStream_t st) {
   const DecodeArgs& a = bt.a[0];
-  decode_score_batch_kernel<<<dim3(nsplit, a.B * a.S_q, bt.L), DEC_THREADS, 0, st>>>(bt);
+  const dim3 g1(nsplit, a.B * a.S_q, bt.L);
+  if (a.chunk == DEC_CHUNK_LONG) decode_score_batch_kernel<DEC_CHUNK_LONG><<<g1, DEC_THREADS, 0, st>>>(bt);
+  else decode_score_batch_kernel<DEC_CHUNK><<<g1, DEC_THREADS, 0, st>>>(bt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_select_batch_kernel<<<dim3(a.B * a.S_q, 1, bt.L), DEC_SEL_THREADS, 0, st>>>(bt);
@@ -1551,7 +1556,8 @@ hipError_t launch_decode_batch(const DecodeBatch& bt, int nsplit, hipStream_t st
 
 hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st) {
   dim3 g1(nsplit, a.B * a.S_q);
-  decode_score_kernel<<<g1, DEC_THREADS, 0, st>>>(a);
+  if (a.chunk == DEC_CHUNK_LONG) decode_score_kernel<DEC_CHUNK_LONG><<<g1, DEC_THREADS, 0, st>>>(a);
+  else decode_score_kernel<DEC_CHUNK><<<g1, DEC_THREADS, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_select_kernel<<<a.B * a.S_q, DEC_SEL_THREADS, 0, st>>>(a);

@@ -149,3 +149,17 @@ def test_decode_all_scores_equal():
     for b in range(p["B"]):
         assert sorted(idx[b, 0].tolist()) == list(range(p["topk"]))
         assert (sc[b, 0] == sc[b, 0, 0]).all()
+
+
+def test_decode_long_chunks_exact_with_ragged_rows():
+    """32 rows against T=32768 with k=2048 take the 2048-key scan chunks; with
+    kv_len some rows are shorter than 8k (their waves cannot vouch for a tight
+    bound, so the select runs over the dense scores), some end inside a chunk.
+    Integer inputs: sets and scores must equal the oracle's exactly."""
+    p = _integer_decode(B=16, S_q=2, T=32768, topk=2048, seed=61)
+    p["kv_len"] = np.array([32768, 5000, 20000, 16384, 16383, 2047, 30001, 8192,
+                            32768, 12345, 24576, 4097, 32000, 2049, 18000, 32767], dtype=np.int32)
+    _say("decode long chunks: B=16 S_q=2 T=32768 k=2048, ragged kv_len")
+    ref_i, ref_s, _ = oracle.oracle_topk(p)
+    idx, sc = _decode(p, return_scores=True)
+    check_exact(idx, ref_i, sc, ref_s)
