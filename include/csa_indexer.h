@@ -41,6 +41,12 @@
  *    otherwise); it needs no initialisation and its contents are undefined
  *    after the call.  ws may be NULL when that size is 0.
  *  - Calls that share a workspace must not overlap (same stream = safe).
+ *  - Library state.  Besides the thread-local error string the library keeps
+ *    (a) a per-device count of resident prefill workgroups per compute unit,
+ *    asked once per device and kernel variant from the HIP occupancy API and
+ *    only read afterwards (a mutex guards the first fill), and (b) the test
+ *    options of csa_set_test_option.  Entry points are otherwise stateless
+ *    and may be called from several threads on different streams.
  */
 #ifndef CSA_INDEXER_H
 #define CSA_INDEXER_H
@@ -125,8 +131,8 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
                                  void* hip_stream);
 
 /* Sigmoid-threshold selection (FlashMemory-DeepSeek-V4 review, "What carries
- * the argument": the Memory Indexer keeps keys whose sigmoid score passes a
- * fixed 0.5 threshold instead of a fixed top-k).  Read as
+ * the argument": in place of a top-k of fixed size, its Memory Indexer keeps
+ * every key whose score, after a sigmoid, is above 0.5).  Read as
  * sigmoid(I + logit_bias) > prob_threshold, i.e. I > logit(tau) - bias
  * (strict), decided on the fp32 score.  0 < prob_threshold < 1.
  * out_count [B, S_q] int32: the true number of survivors (may exceed cap).
@@ -239,6 +245,24 @@ csa_status csa_project(const void* x, const void* w, int64_t M, int32_t N, int32
 #define CSA_MAX_UNION_T (1 << 20)
 csa_status csa_union_rows(const int32_t* const* lists, const int32_t* widths, int32_t L, int64_t rows,
                           int32_t T, int32_t cap, int32_t* out_idx, int32_t* out_count, void* hip_stream);
+
+/* Test options: process-wide switches that let tests drive every code path
+ * from one process.  They change which kernel variant runs or how often the
+ * prefill candidate lists are compacted, never the results; all are 0 (off,
+ * automatic) at load.  Not meant for production use; set them only while no
+ * other thread is inside a library call.
+ *   CSA_OPT_FORCE_GENERIC  1: every prefill-family call uses the generic
+ *                          kernel (one score per lane, fp32 FMAs in index
+ *                          order), also for bf16 H = 64, D = 128.
+ *   CSA_OPT_CAND_CAP       > 0: candidate keys held per query row between
+ *                          compactions of the prefill kernels (raised to the
+ *                          minimum 2*k + 64 when smaller); 0: 4*k + 64.
+ *   CSA_OPT_DECODE_CHUNK   1024 or 2048: keys per decode-scan workgroup;
+ *                          0: chosen from the shape.
+ * Errors: CSA_ERR_INVALID for an unknown option or a value outside its range
+ * (the option keeps its value). */
+enum { CSA_OPT_FORCE_GENERIC = 1, CSA_OPT_CAND_CAP = 2, CSA_OPT_DECODE_CHUNK = 3 };
+csa_status csa_set_test_option(int32_t option, int64_t value);
 
 const char* csa_status_str(csa_status s); /* static string, never NULL */
 const char* csa_last_error(void);         /* thread-local detail of this thread's last error */

@@ -12,5 +12,5 @@ from ._binding import (  # noqa: F401
     load_library, make_problem, set_recall, version, workspace_size,
     CsaAttnProblem, attention_workspace_size, make_attn_problem, sparse_attention, union_rows,
     MultiLayerSelector, MAX_LAYERS, batchable_layers, index_threshold_select_layers, MultiLayerIndexer,
-    project, query_projection, head_weight_projection, compress_keys,
+    project, query_projection, head_weight_projection, compress_keys, test_options,
 )

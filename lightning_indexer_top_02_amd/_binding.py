@@ -70,6 +70,7 @@ _SIGS = {
     "csa_union_rows": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, ctypes.c_int64, _i32, _i32, _vp,
                               _vp, _vp]),
     "csa_project": (_i32, [_vp, _vp, ctypes.c_int64, _i32, _i32, _i32, _vp, _vp]),
+    "csa_set_test_option": (_i32, [_i32, ctypes.c_int64]),
     "csa_status_str": (ctypes.c_char_p, [_i32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_version": (ctypes.c_int, []),
@@ -104,6 +105,39 @@ def _check(status):
 
 def version() -> int:
     return load_library().csa_version()
+
+
+CSA_OPT_FORCE_GENERIC, CSA_OPT_CAND_CAP, CSA_OPT_DECODE_CHUNK = 1, 2, 3
+_TEST_OPTIONS = {"force_generic": CSA_OPT_FORCE_GENERIC, "cand_cap": CSA_OPT_CAND_CAP,
+                 "decode_chunk": CSA_OPT_DECODE_CHUNK}
+
+
+class test_options:
+    """Context manager over csa_set_test_option: e.g.
+    ``with test_options(cand_cap=1): ...`` forces the prefill kernels to
+    compact their candidate lists on almost every key tile; the options go
+    back to 0 (automatic) on exit.  For tests: the options change which
+    kernel variant runs, never the results."""
+
+    __test__ = False                                   # not a pytest class
+
+    def __init__(self, **opts):
+        unknown = set(opts) - set(_TEST_OPTIONS)
+        if unknown:
+            raise ValueError(f"unknown test options {sorted(unknown)}")
+        self.opts = opts
+
+    def __enter__(self):
+        lib = load_library()
+        for name, val in self.opts.items():
+            _check(lib.csa_set_test_option(_TEST_OPTIONS[name], int(val)))
+        return self
+
+    def __exit__(self, *exc):
+        lib = load_library()
+        for name in self.opts:
+            lib.csa_set_test_option(_TEST_OPTIONS[name], 0)
+        return False
 
 
 # ---------------------------------------------------------------------------

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -42,10 +44,10 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // per row of `threads` threads allows at most this many rows.
 long long max_rows_per_dispatch(int threads) { return ((1ll << 32) - 1) / threads; }
 
-bool env_is(const char* name, const char* val) {
-  const char* e = std::getenv(name);
-  return e && std::strcmp(e, val) == 0;
-}
+// Test options (csa_set_test_option): process-wide, 0 = default behaviour.
+std::atomic<long long> g_opt_force_generic{0};
+std::atomic<long long> g_opt_cand_cap{0};
+std::atomic<long long> g_opt_decode_chunk{0};
 
 csa_status validate_problem(const csa_problem* p) {
   if (!p) return fail(CSA_ERR_INVALID, "problem pointer is NULL");
@@ -78,7 +80,7 @@ csa_status validate_k(int32_t k, const char* what) {
 }
 
 bool use_mfma(const csa_problem* p) {
-  if (env_is("CSA_FORCE_PATH", "generic")) return false;
+  if (g_opt_force_generic.load(std::memory_order_relaxed)) return false;
   return p->dtype == CSA_BF16 && p->H == 64 && p->D == 128;
 }
 
@@ -87,30 +89,34 @@ bool use_mfma(const csa_problem* p) {
 // 2k + 64 (every compaction select then fits the registers for k <= 2048),
 // but long rows compact less often with the larger buffer and run faster
 // (S=65536, T=16384, k=2048: 11.1 -> 10.3 ms), while rows of at most 4k
-// visible keys never compact at either size.  CSA_CAND_CAP overrides (tests
-// use it to force frequent compactions); it is clamped to the minimum.
+// visible keys never compact at either size.  The CSA_OPT_CAND_CAP test
+// option overrides it (tests force frequent compactions); it is clamped to
+// the minimum.
 int cand_capacity(int kk) {
   const int lo = 2 * kk + 64;
   long long c = 4ll * kk + 64;
-  if (const char* e = std::getenv("CSA_CAND_CAP")) {
-    long long v = std::atoll(e);
-    if (v > 0) c = std::max<long long>(v, lo);
-  }
+  const long long v = g_opt_cand_cap.load(std::memory_order_relaxed);
+  if (v > 0) c = std::max<long long>(v, lo);
   return (int)((c + 63) / 64 * 64);
 }
 
 struct PrefillPlan {
-  int nqb, n_items, ws_slots, C;
+  int nqb, ws_slots, C;
+  long long n_items;
   size_t cand_bytes, sort_bytes, total;
 };
+
+// Work items (query blocks x partitions) one prefill launch can index: the
+// kernels count rounds of the persistent grid in 32-bit ints.
+constexpr long long PF_MAX_ITEMS = (long long)INT_MAX - csa::PF_MAX_GRID;
 
 // Workspace layout: [ws_slots workgroups x PF_ROWS candidate buffers of C
 // keys][sort scratch when CSA_SORTED].
 PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, uint32_t flags) {
   PrefillPlan pl;
   pl.nqb = (p->S_q + csa::PF_ROWS - 1) / csa::PF_ROWS;
-  long long items = (long long)p->B * pl.nqb * P;
-  pl.n_items = (int)std::min<long long>(items, (1ll << 31) - 1);
+  const long long items = (long long)p->B * pl.nqb * P;
+  pl.n_items = items;
   pl.ws_slots = (int)std::min<long long>(items, csa::PF_MAX_GRID);
   pl.C = cand_capacity(kk);
   pl.cand_bytes = align_up((size_t)pl.ws_slots * csa::PF_ROWS * pl.C * sizeof(unsigned long long));
@@ -135,6 +141,8 @@ struct DecodePlan {
 // has two workgroups per CU of an MI355X (256 CUs); else 1024.  Measured at
 // B=32, T=32768, k=2048: 61.7 -> 60.4 us per decode call.
 int decode_chunk(const csa_problem* p, int kk) {
+  const long long forced = g_opt_decode_chunk.load(std::memory_order_relaxed);
+  if (forced == csa::DEC_CHUNK || forced == csa::DEC_CHUNK_LONG) return (int)forced;
   const long long rows = (long long)p->B * p->S_q;
   const long long wgs = rows * ((p->T + csa::DEC_CHUNK_LONG - 1) / csa::DEC_CHUNK_LONG);
   return (8ll * kk <= p->T && wgs >= 512) ? csa::DEC_CHUNK_LONG : csa::DEC_CHUNK;
@@ -175,13 +183,18 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
                               int32_t* out_count, void* ws, size_t ws_bytes, void* stream) {
   const int out_stride = kk * P;
   const PrefillPlan pl = plan_prefill(p, kk, P, out_stride, flags);
+  if (pl.n_items > PF_MAX_ITEMS)
+    return fail(CSA_ERR_UNSUPPORTED, "B * ceil(S_q/%d) * P = %lld query blocks above %lld per call", csa::PF_ROWS,
+                pl.n_items, PF_MAX_ITEMS);
+  const bool sorted = (flags & CSA_SORTED) != 0;
+  const long long sort_rows = (long long)p->B * p->S_q * P;     // one sort workgroup per output row segment
+  if (sorted && sort_rows > max_rows_per_dispatch(256))
+    return fail(CSA_ERR_UNSUPPORTED, "CSA_SORTED supports at most %lld output rows (B*S_q*P = %lld)",
+                max_rows_per_dispatch(256), sort_rows);
   if (ws_bytes < pl.total || (pl.total > 0 && !ws))
     return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, pl.total);
   if ((uintptr_t)ws % 16) return fail(CSA_ERR_INVALID, "workspace must be 16-byte aligned");
   const bool mfma = use_mfma(p);
-  const bool sorted = (flags & CSA_SORTED) != 0;
-  if (sorted && (long long)p->B * p->S_q > max_rows_per_dispatch(256))
-    return fail(CSA_ERR_UNSUPPORTED, "CSA_SORTED supports at most %lld query rows", max_rows_per_dispatch(256));
   float* score_dst = out_score;
   if (sorted && !score_dst) score_dst = (float*)((char*)ws + pl.cand_bytes);
 
@@ -190,7 +203,7 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
   a.B = p->B; a.S_q = p->S_q; a.T = p->T; a.H = p->H; a.D = p->D; a.m = p->m;
   a.q_pos0 = p->q_pos0;
   a.causal = (flags & CSA_NONCAUSAL) ? 0 : 1;
-  a.kk = kk; a.P = P; a.nqb = pl.nqb; a.n_items = pl.n_items;
+  a.kk = kk; a.P = P; a.nqb = pl.nqb; a.n_items = (int)pl.n_items;
   a.thr_fixed = thr_fixed;
   a.out_idx = out_idx; a.out_score = score_dst; a.out_count = out_count;
   a.out_stride = out_stride;
@@ -205,7 +218,7 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
   hipError_t e = csa::launch_prefill(a, mode, mfma, grid, st);
   if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   if (sorted) {
-    e = csa::launch_sort_rows(out_idx, score_dst, (long long)p->B * p->S_q * P, kk, st);
+    e = csa::launch_sort_rows(out_idx, score_dst, sort_rows, kk, st);
     if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "sort launch failed: %s", hipGetErrorString(e));
   }
   return ok();
@@ -227,6 +240,25 @@ const char* csa_status_str(csa_status s) {
 }
 
 const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+csa_status csa_set_test_option(int32_t option, int64_t value) {
+  switch (option) {
+    case CSA_OPT_FORCE_GENERIC:
+      if (value != 0 && value != 1) return fail(CSA_ERR_INVALID, "CSA_OPT_FORCE_GENERIC takes 0 or 1");
+      g_opt_force_generic.store(value);
+      return ok();
+    case CSA_OPT_CAND_CAP:
+      if (value < 0 || value > (1ll << 30)) return fail(CSA_ERR_INVALID, "CSA_OPT_CAND_CAP outside [0, 2^30]");
+      g_opt_cand_cap.store(value);
+      return ok();
+    case CSA_OPT_DECODE_CHUNK:
+      if (value != 0 && value != csa::DEC_CHUNK && value != csa::DEC_CHUNK_LONG)
+        return fail(CSA_ERR_INVALID, "CSA_OPT_DECODE_CHUNK takes 0, %d or %d", csa::DEC_CHUNK, csa::DEC_CHUNK_LONG);
+      g_opt_decode_chunk.store(value);
+      return ok();
+  }
+  return fail(CSA_ERR_INVALID, "unknown test option %d", option);
+}
 
 int csa_version(void) { return 100; }   // 0.1.0
 

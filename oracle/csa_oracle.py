@@ -27,9 +27,9 @@ the Multi-layer Indexer blog post):
 * Selection is an exact top-k with ties broken toward the lower key index;
   the materialise-then-top-k path is the ground truth the streaming method
   must match (StreamIndex abstract: set-overlap recall is bit-exact at small S).
-* Threshold variant: FlashMemory's Memory Indexer keeps a key when the
-  sigmoid of its score exceeds a fixed 0.5 instead of taking a fixed top-k
-  ("What carries the argument"; free parameter "classification threshold").
+* Threshold variant: rather than a top-k of fixed size, FlashMemory's Memory
+  Indexer keeps each key whose sigmoid-mapped score lies above 0.5 ("What
+  carries the argument"; free parameter "classification threshold").
   Read as sigma(I + bias) > tau, i.e. I > logit(tau) - bias, strict.
 * Interleaved variant: Interleaved DeepSeek Sparse Attention places tokens
   in an interleaved layout across devices; each device selects locally and

@@ -262,3 +262,40 @@ def test_project_argument_errors(lib):
     assert call(x=0x1008) == Bd.CSA_ERR_INVALID                     # 16-byte alignment
     assert call(dt=Bd.CSA_F32, y=0x3002) == Bd.CSA_ERR_INVALID
     assert call(M=0, x=None, w=None, y=None) == Bd.CSA_OK           # nothing to do
+
+
+def test_test_options(lib):
+    """csa_set_test_option: valid values accepted, others rejected with the
+    option unchanged; the binding's context manager resets to 0."""
+    for opt, good, bad in [(Bd.CSA_OPT_FORCE_GENERIC, [0, 1], [2, -1]),
+                           (Bd.CSA_OPT_CAND_CAP, [0, 1, 1 << 20], [-1, (1 << 30) + 1]),
+                           (Bd.CSA_OPT_DECODE_CHUNK, [0, 1024, 2048], [512, 4096, 1])]:
+        for v in good:
+            assert lib.csa_set_test_option(opt, v) == Bd.CSA_OK
+        for v in bad:
+            assert lib.csa_set_test_option(opt, v) == Bd.CSA_ERR_INVALID
+            assert lib.csa_last_error().decode()
+        assert lib.csa_set_test_option(opt, 0) == Bd.CSA_OK
+    assert lib.csa_set_test_option(99, 0) == Bd.CSA_ERR_INVALID
+    p = _prob(S_q=256)
+    base = Bd.workspace_size(Bd.OP_PREFILL, p, 64)
+    with L.test_options(cand_cap=4096):                  # larger candidate buffers need more workspace
+        assert Bd.workspace_size(Bd.OP_PREFILL, p, 64) > base
+    assert Bd.workspace_size(Bd.OP_PREFILL, p, 64) == base
+    with pytest.raises(ValueError):
+        L.test_options(no_such_option=1)
+
+
+def test_prefill_size_limits_reject_before_enqueue(lib):
+    """Work the kernels cannot index is refused with CSA_ERR_UNSUPPORTED before
+    anything is enqueued (the pointers here are never dereferenced)."""
+    # B * ceil(S_q / 4) * P query blocks above what one launch counts in 32 bits
+    p = _prob(S_q=1 << 30, T=1 << 20)
+    assert lib.csa_index_topk_interleaved(ctypes.byref(p), 16, 1, 0, 0x4000, None, 0x5000, 1 << 60,
+                                          None) == Bd.CSA_ERR_UNSUPPORTED
+    assert "query blocks" in lib.csa_last_error().decode()
+    # CSA_SORTED launches one sort workgroup per output row segment (B * S_q * P)
+    p = _prob(S_q=1 << 22, T=1 << 20)
+    assert lib.csa_index_topk_interleaved(ctypes.byref(p), 8, 1, Bd.CSA_SORTED, 0x4000, None, 0x5000, 1 << 60,
+                                          None) == Bd.CSA_ERR_UNSUPPORTED
+    assert "CSA_SORTED" in lib.csa_last_error().decode()
