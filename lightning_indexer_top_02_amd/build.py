@@ -17,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa_indexer.so")
 SOURCES = ["csa_kernels.hip", "csa_api.cpp"]
+# measurement aid for the benchmark (a plain streaming read), not part of the ABI
+CALIB_LIB = os.path.join(HERE, "libcsa_calib.so")
+CALIB_SOURCES = ["csa_calib.hip"]
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -27,8 +30,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the CSA indexer library)")
 
 
-def command(out: str = LIB) -> list:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def command(out: str = LIB, sources=SOURCES) -> list:
+    srcs = [os.path.join(CSRC, s) for s in sources]
     return [
         hipcc(), "-O3", "-std=c++17", "-fPIC", "-shared",
         f"--offload-arch={ARCH}",
@@ -40,9 +43,9 @@ def command(out: str = LIB) -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _compile(out: str, sources, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = command(tmp, sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,7 +56,12 @@ def build(verbose: bool = False) -> str:
     for line in (res.stdout + res.stderr).splitlines():
         if line.strip() and noise not in line and verbose:
             print(line)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(LIB, SOURCES, verbose)
+    _compile(CALIB_LIB, CALIB_SOURCES, verbose)
     return LIB
 
 

@@ -53,3 +53,18 @@ def attention_bytes(rows: int, n_valid: int, H: int, Dk: int, Dv: int, n_sel: in
 def materialised_score_bytes(B: int, S: int, H: int, T: int) -> int:
     """Size of the fp32 [B, S, H_I, T] score tensor the streaming method avoids."""
     return B * S * H * T * 4
+
+
+def interleaved_pairs(S_q: int, q_pos0: int, m: int, T: int, P: int, k_local: int, causal: bool = True,
+                      B: int = 1) -> int:
+    """Needed (query, key) pairs of the interleaved variant: partition p of a
+    row holds its visible keys s = p, p+P, ...; a partition with at most
+    k_local of them keeps them all and needs no score."""
+    need = 0
+    for i in range(S_q):
+        v = row_visible(q_pos0 + i, m, T, causal)
+        for p in range(P):
+            n = (v - p + P - 1) // P if v > p else 0
+            if n > k_local:
+                need += n
+    return need * B
