@@ -163,3 +163,26 @@ def test_decode_long_chunks_exact_with_ragged_rows():
     ref_i, ref_s, _ = oracle.oracle_topk(p)
     idx, sc = _decode(p, return_scores=True)
     check_exact(idx, ref_i, sc, ref_s)
+
+
+def test_decode_chunk_sizes_same_sets():
+    """The decode scan split into 1024-key and into 2048-key workgroup chunks
+    gives the same sets and bitwise the same scores on one input (the config-4
+    decode shape, all 32 rows), and integer inputs match the oracle exactly at
+    both chunk sizes."""
+    p = csa_inputs.config(4)
+    _say("decode chunk invariance: config 4 with 1024- and 2048-key chunks")
+    with L.test_options(decode_chunk=1024):
+        a, sa = _decode(p, return_scores=True)
+    with L.test_options(decode_chunk=2048):
+        b, sb = _decode(p, return_scores=True)
+    for bb in range(p["B"]):
+        ma = dict(zip(a[bb, 0].tolist(), sa[bb, 0].view(np.uint32).tolist()))
+        mb = dict(zip(b[bb, 0].tolist(), sb[bb, 0].view(np.uint32).tolist()))
+        assert ma == mb, f"sequence {bb}: chunk sizes disagree"
+    q = _integer_decode(B=4, S_q=2, T=20000, topk=1000, seed=71)
+    ref_i, ref_s, _ = oracle.oracle_topk(q)
+    for ch in (1024, 2048):
+        with L.test_options(decode_chunk=ch):
+            idx, sc = _decode(q, return_scores=True)
+        check_exact(idx, ref_i, sc, ref_s)

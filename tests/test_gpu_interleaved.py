@@ -9,7 +9,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import lightning_indexer_top_02_amd as L  # noqa: E402
-from gpu_common import check_exact, check_tolerance, to_device  # noqa: E402
+from gpu_common import check_exact, check_tolerance, map_rows, to_device  # noqa: E402
 
 
 def _say(msg):
@@ -65,27 +65,42 @@ def test_recall_kernel_edge_cases():
     assert rec.tolist() == [1.0, 0.5, 1.0, 1.0]
 
 
-def test_config5_interleaved_recall_sampled():
+def test_config5_interleaved_256_rows_and_recall_every_row():
+    """Million-token tail, P=8 strided partitions with a local top-320 each:
+    256 seeded rows (first and last included) against the oracle's per-partition
+    selection under the bf16 tolerance rule; on every one of the 8192 rows the
+    union's recall of the global top-2048 equals the closed form
+    sum_p min(c_p, 320) / 2048 (c_p = global top-k members in partition p),
+    and it stays at or above the pages' minimum of 0.998."""
     p = csa_inputs.config(5)
-    rows = csa_inputs.sample_rows(p["S_q"], 6, seed=55, must=(8191,))
-    _say("config 5 interleaved P=8 k_local=320 vs global top-2048")
+    P, kl = 8, 320
+    rows = csa_inputs.sample_rows(p["S_q"], 256, seed=55, must=(0, p["S_q"] - 1))
+    _say("config 5 interleaved P=8 k_local=320: 256 seeded rows vs the oracle, recall on all 8192 rows")
     q, k, w, _ = to_device(p)
-    il = L.index_topk_interleaved(q, k, w, 8, 320, m=4, q_pos0=p["q_pos0"])
+    il = L.index_topk_interleaved(q, k, w, P, kl, m=4, q_pos0=p["q_pos0"])
     glob = L.index_topk_prefill(q, k, w, 2048, m=4, q_pos0=p["q_pos0"])
-    rec = L.set_recall(il, glob, p["T"]).cpu().numpy()
-    _say(f"  recall mean={rec.mean():.6f} min={rec.min():.6f}")
+    rec = L.set_recall(il, glob, p["T"]).cpu().numpy().astype(np.float64)
+    g = glob.cpu().numpy()[0]
+    cnt = np.stack([(g % P == part).sum(1) for part in range(P)], 1)
+    closed = np.minimum(cnt, kl).sum(1) / g.shape[1]
+    assert np.array_equal(rec.astype(np.float32), closed.astype(np.float32)), "recall differs from the closed form"
+    _say(f"  recall mean={rec.mean():.7f} min={rec.min():.6f}; {(cnt > kl).sum()} of {cnt.size} row-partitions drop")
+    assert rec.min() >= 0.998 and rec.mean() >= 0.9999
     il_np = il.cpu().numpy()
     scorer = oracle.RowScorer(p)
-    ref = oracle.oracle_interleaved(p, 8, 320, rows=rows)[0]
-    for r_i, r in enumerate(rows):
+
+    def one(ri):
+        r = int(rows[ri])
         I = scorer(0, r)
-        for part in range(8):
-            seg = il_np[0, r, part * 320:(part + 1) * 320]
-            rseg = ref[0, r_i, part * 320:(part + 1) * 320]
-            assert (seg >= 0).all() and (seg % 8 == part).all()
-            sub = np.arange(part, I.shape[0], 8)
+        floor = float(np.sqrt(np.mean(I * I))) / 256
+        for part in range(P):
+            seg = il_np[0, r, part * kl:(part + 1) * kl]
+            sub = np.arange(part, I.shape[0], P)
+            rseg = sub[oracle.select_topk(I[sub], kl)]
+            assert (seg >= 0).all() and (seg % P == part).all() and len(set(seg.tolist())) == kl
             vn = I[rseg].min()
-            floor = float(np.sqrt(np.mean(I * I))) / 256
             for s in set(seg.tolist()) ^ set(rseg.tolist()):
-                assert abs(I[s] - vn) <= 2e-3 * max(abs(vn), floor)
-    assert rec.min() >= 0.99
+                assert abs(I[s] - vn) <= 2e-3 * max(abs(vn), floor), f"row {r} partition {part}: index {s}"
+        return 1
+
+    assert sum(map_rows(one, range(len(rows)), say=_say, chunk=128)) == len(rows)

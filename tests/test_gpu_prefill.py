@@ -1,6 +1,4 @@
 """GPU parity of csa_index_topk_prefill against the CPU oracle (through the C ABI)."""
-import os
-
 import numpy as np
 import pytest
 
@@ -28,22 +26,6 @@ def _run(prob, topk=None, rows=None, **kw):
         idx, sc = out
         return idx.cpu().numpy(), sc.cpu().numpy()
     return out.cpu().numpy(), None
-
-
-class _Env:
-    def __init__(self, **kv):
-        self.kv = kv
-
-    def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.kv}
-        os.environ.update({k: str(v) for k, v in self.kv.items()})
-
-    def __exit__(self, *a):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
 
 
 def test_config1_bit_exact():
@@ -82,7 +64,7 @@ def test_mfma_integer_bit_exact_and_generic_invariance():
     ref_i, ref_s, _ = oracle.oracle_topk(p)
     idx, sc = _run(p, return_scores=True)
     check_exact(idx, ref_i, sc, ref_s)
-    with _Env(CSA_FORCE_PATH="generic"):
+    with L.test_options(force_generic=1):
         idx_g, sc_g = _run(p, return_scores=True)
     check_exact(idx_g, ref_i, sc_g, ref_s)
 
@@ -92,7 +74,7 @@ def test_compaction_invariance_integer():
     p = _integer_bf16(S_q=96, T=2000, topk=100, q_pos0=6000, qr=1, wr=1, seed=5)
     ref_i, ref_s, _ = oracle.oracle_topk(p)
     idx_a, sc_a = _run(p, return_scores=True)
-    with _Env(CSA_CAND_CAP="1"):
+    with L.test_options(cand_cap=1):
         idx_b, sc_b = _run(p, return_scores=True)
     check_exact(idx_a, ref_i, sc_a, ref_s)
     check_exact(idx_b, ref_i, sc_b, ref_s)
@@ -115,7 +97,7 @@ def test_determinism_and_compaction_same_sets():
     a, sa = _run(p, return_scores=True)
     b, sb = _run(p, return_scores=True)
     assert (a == b).all() and (sa.view(np.uint32) == sb.view(np.uint32)).all()
-    with _Env(CSA_CAND_CAP="1"):
+    with L.test_options(cand_cap=1):
         c, sc_ = _run(p, return_scores=True)
     for r in range(a.shape[1]):
         assert sorted(a[0, r].tolist()) == sorted(c[0, r].tolist())
@@ -155,38 +137,57 @@ def test_edge_cases_exact(case):
         assert not np.signbit(sc[sc == 0]).any()
 
 
-def test_config2_full_size_sampled_rows():
+def test_config2_full_size_every_row():
+    """V4-Flash prefill at full size (S=16384, T=4096, k=2048): every query
+    row, indices and scores, under the bf16 tolerance rule."""
     p = csa_inputs.config(2)
-    rows = csa_inputs.sample_rows(p["S_q"], 48, seed=2, must=(0, 8187, 8188, 8191, 8192, 8195, 16383))
-    _say("config 2 full size (S=16384 T=4096 k=2048), 48 sampled rows")
+    _say("config 2 full size (S=16384 T=4096 k=2048): all 16384 rows")
     idx, sc = _run(p, return_scores=True)
-    st = check_tolerance(p, rows, idx[:, rows], sc[:, rows], p["topk"])
+    st = check_tolerance(p, np.arange(p["S_q"]), idx, sc, p["topk"], say=_say)
+    assert st["rows"] == p["S_q"]
     _say(f"  boundary swaps={st['swaps']} max rel err={st['max_rel']:.2e}")
-    idx2, _ = _run(p)
-    check_tolerance(p, rows, idx2[:, rows], None, p["topk"])
+    idx2, _ = _run(p)                              # index-only launch: the same sets
+    for r in range(p["S_q"]):
+        assert set(idx2[0, r].tolist()) == set(idx[0, r].tolist()), f"row {r}: index-only run differs"
 
 
-def test_config3_long_prefill_sampled_rows():
+def _tail_rows(S_q, n, seed, k, m=4, q_pos0=0):
+    """n seeded rows that always include the first and last rows and, when the
+    range has them, the rows around vis = k (the last rows that copy their
+    visible keys and the first that need a selection)."""
+    must = [0, S_q - 1]
+    for i in range(S_q):
+        v = (q_pos0 + i) // m + 1
+        if k - 1 <= v <= k + 1:
+            must.append(i)
+    return csa_inputs.sample_rows(S_q, n, seed=seed, must=must)
+
+
+def test_config3_long_prefill_1024_rows():
     p = csa_inputs.config(3)
-    rows = csa_inputs.sample_rows(p["S_q"], 24, seed=3, must=(0, 8191, 8192, 65535))
-    _say("config 3 long prefill (S=65536 T=16384), 24 sampled rows")
-    idx, _ = _run(p)
-    check_tolerance(p, rows, idx[:, rows], None, p["topk"])
+    rows = _tail_rows(p["S_q"], 1024, 3, p["topk"])
+    assert 8191 in rows and 8192 in rows and len(rows) == 1024
+    _say("config 3 long prefill (S=65536 T=16384), 1024 seeded rows incl. first, last and vis = k")
+    idx, sc = _run(p, return_scores=True)
+    st = check_tolerance(p, rows, idx[:, rows], sc[:, rows], p["topk"], say=_say)
+    _say(f"  boundary swaps={st['swaps']} max rel err={st['max_rel']:.2e}")
 
 
-def test_config5_million_token_tail_sampled_rows():
+def test_config5_million_token_tail_1024_rows():
     p = csa_inputs.config(5)
-    rows = csa_inputs.sample_rows(p["S_q"], 12, seed=5, must=(0, 8191))
-    _say("config 5 tail (S_q=8192 of 1M, T=262144), 12 sampled rows")
-    idx, _ = _run(p)
-    check_tolerance(p, rows, idx[:, rows], None, p["topk"])
+    rows = _tail_rows(p["S_q"], 1024, 5, p["topk"], q_pos0=p["q_pos0"])
+    assert rows[0] == 0 and rows[-1] == p["S_q"] - 1 and len(rows) == 1024
+    _say("config 5 tail (S_q=8192 of 1M, T=262144), 1024 seeded rows incl. first and last")
+    idx, sc = _run(p, return_scores=True)
+    st = check_tolerance(p, rows, idx[:, rows], sc[:, rows], p["topk"], say=_say)
+    _say(f"  boundary swaps={st['swaps']} max rel err={st['max_rel']:.2e}")
 
 
 @pytest.mark.parametrize("case", ["compaction", "ragged", "kvlen_batch", "topk_gt_T", "many_items",
                                   "long_cand_list"])
 def test_mfma_paths_exact(case):
     """The MFMA prefill kernel returns the oracle's sets on every path of its
-    candidate lists: default capacity and the smallest one (CSA_CAND_CAP=1:
+    candidate lists: default capacity and the smallest one (cand_cap=1:
     compactions on almost every tile), several query blocks per workgroup,
     and lists longer than the final select's registers (k = 2200)."""
     if case == "compaction":        # 24 key tiles per row
@@ -204,9 +205,28 @@ def test_mfma_paths_exact(case):
         p = _integer_bf16(S_q=8, T=6000, topk=2200, q_pos0=4 * 5990, seed=9)
     _say(f"mfma prefill paths: {case}")
     ref_i, ref_s, _ = oracle.oracle_topk(p)
-    for env in ({}, {"CSA_CAND_CAP": "1"}):
-        with _Env(**env):
+    for opts in ({}, {"cand_cap": 1}):
+        with L.test_options(**opts):
             idx, sc = _run(p, return_scores=True)
             idx2, _ = _run(p)
         check_exact(idx, ref_i, sc, ref_s)
         check_exact(idx2, ref_i)
+
+
+@pytest.mark.parametrize("topk", [64, 512, 2048, 4096])
+def test_topk_sweep_exact_integer(topk):
+    """The pages sweep top-k among their selection parameters: k = 64 ... 4096
+    (the library's largest) on integer-valued bf16 inputs at the MFMA shape,
+    rows of about 6000 visible keys; prefill and decode entry points both
+    return the oracle's sets and scores exactly."""
+    p = _integer_bf16(S_q=48, T=6000, topk=topk, q_pos0=4 * 5980, seed=200 + topk // 64)
+    _say(f"top-k sweep k={topk}: prefill S_q=48, T=6000")
+    ref_i, ref_s, _ = oracle.oracle_topk(p)
+    idx, sc = _run(p, return_scores=True)
+    check_exact(idx, ref_i, sc, ref_s)
+    d = _integer_bf16(S_q=2, T=12000, topk=topk, q_pos0=4 * 12000 - 2, seed=300 + topk // 64, B=3)
+    q, k, w, _ = to_device(d)
+    di, ds = L.index_topk_decode(q, k, w, topk, m=4, q_pos0=d["q_pos0"], return_scores=True)
+    torch.cuda.synchronize()
+    rd_i, rd_s, _ = oracle.oracle_topk(d)
+    check_exact(di.cpu().numpy(), rd_i, ds.cpu().numpy(), rd_s)

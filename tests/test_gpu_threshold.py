@@ -54,22 +54,46 @@ def test_threshold_half_is_sign_test():
         assert cnt[0, r] == int((I > 0).sum())
 
 
-def test_threshold_bf16_gaussian_tolerance():
+@pytest.mark.parametrize("cap", [512, 40])
+def test_threshold_bf16_gaussian_tolerance(cap):
+    """Gaussian bf16 inputs: the count, the returned scores and the kept set
+    under the bf16 tolerance rule.  With cap = 512 most rows keep every
+    survivor; with cap = 40 most rows truncate, and the kept keys must be the
+    survivors' best 40 by score (up to the band around the 40th)."""
     p = csa_inputs.make_gaussian_bf16(1, 256, 2048, 64, 128, 4, 512, q_pos0=7000, seed=17)
-    tau, bias, cap = 0.5, -0.05, 512
+    tau, bias = 0.5, -0.05
     idx, cnt, sc = _thr(p, cap, tau, bias)
     theta = oracle.logit_threshold(tau, bias)
     scorer = oracle.RowScorer(p)
+    truncated = 0
     for r in range(p["S_q"]):
         I = scorer(0, r)
         floor = float(np.sqrt(np.mean(I * I))) / FLOOR_DIV
         band = REL * max(abs(theta), floor)
         near = int((np.abs(I - theta) <= band).sum())
-        assert abs(int(cnt[0, r]) - int((I > theta).sum())) <= near
+        true_cnt = int((I > theta).sum())
+        assert abs(int(cnt[0, r]) - true_cnt) <= near
         n = min(cap, int(cnt[0, r]))
         sel = idx[0, r, :n]
         assert (idx[0, r, n:] == -1).all() and len(set(sel.tolist())) == n
         assert (I[sel] > theta - band).all()
+        # scores: each within the rule of its oracle score; padding -inf
+        err = np.abs(sc[0, r, :n].astype(np.float64) - I[sel])
+        assert (err <= REL * np.maximum(np.abs(I[sel]), floor)).all(), f"row {r}: score error {err.max()}"
+        assert np.isneginf(sc[0, r, n:]).all()
+        surv = oracle.order_desc(I, np.nonzero(I > theta)[0])
+        if true_cnt > cap:                          # the cap keeps the survivors' best by score
+            truncated += 1
+            ref = surv[:cap]
+            vc = I[ref].min()
+            bc = REL * max(abs(vc), floor)
+            for s_ in set(sel.tolist()) ^ set(ref.tolist()):
+                assert abs(I[s_] - vc) <= bc, f"row {r}: index {s_} outside the band of the cap-th survivor"
+        else:                                       # every survivor kept, up to keys at the threshold
+            for s_ in set(sel.tolist()) ^ set(surv.tolist()):
+                assert abs(I[s_] - theta) <= band, f"row {r}: survivor {s_} missing or extra"
+    if cap == 40:                                   # both branches above are exercised
+        assert p["S_q"] // 2 < truncated < p["S_q"]
 
 
 def test_threshold_nesting_gpu():
