@@ -44,8 +44,9 @@
  *  - Library state.  Besides the thread-local error string the library keeps
  *    (a) a per-device count of resident prefill workgroups per compute unit,
  *    asked once per device and kernel variant from the HIP occupancy API and
- *    only read afterwards (a mutex guards the first fill), and (b) the test
- *    options of csa_set_test_option.  Entry points are otherwise stateless
+ *    only read afterwards (a mutex guards the first fill), (b) the test
+ *    options of csa_set_test_option, and (c) per GPU, the scratch array of
+ *    csa_index_topk_decode_noalloc and its address, looked up once.  Entry points are otherwise stateless
  *    and may be called from several threads on different streams.
  */
 #ifndef CSA_INDEXER_H
@@ -129,6 +130,24 @@ csa_status csa_index_topk_prefill(const csa_problem* prob, int32_t topk, uint32_
 csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t flags,
                                  int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
                                  void* hip_stream);
+
+/* csa_index_topk_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, limits and
+ * results as csa_index_topk_decode; the decode workspace comes from a fixed
+ * scratch array of CSA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends, so the call allocates nothing.
+ * Supported: the decode fast path (bf16 q and k, H = 64, D = 128, S_q <=
+ * CSA_MAX_DECODE_SQ) with a workspace need of at most the scratch size, i.e.
+ * about B*S_q*(T+64)*4 bytes of scores plus 64 bytes per 1024 keys per row
+ * (B*S_q = 32 rows at T = 32768 take 4.2 MB); larger problems and other
+ * shapes return CSA_ERR_UNSUPPORTED with nothing enqueued.  The scratch needs
+ * no initialisation.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap on one GPU (different streams, or other threads) race and
+ * give undefined results; calls in one stream are ordered and safe. */
+#define CSA_NOALLOC_SCRATCH_BYTES (8u << 20)
+csa_status csa_index_topk_decode_noalloc(const csa_problem* prob, int32_t topk, uint32_t flags,
+                                         int32_t* out_idx, float* out_score, void* hip_stream);
 
 /* Sigmoid-threshold selection (FlashMemory-DeepSeek-V4 review, "What carries
  * the argument": in place of a top-k of fixed size, its Memory Indexer keeps

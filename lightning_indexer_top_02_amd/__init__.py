@@ -7,8 +7,8 @@ in include/csa_indexer.h); this package only marshals torch tensors into it.
 """
 from ._binding import (  # noqa: F401
     CSA_BF16, CSA_F32, CSA_NONCAUSAL, CSA_SORTED, EXPORTS, LIB_PATH, MAX_DECODE_SQ, MAX_TOPK,
-    OP_DECODE, OP_INTERLEAVED, OP_PREFILL, OP_RECALL, OP_THRESHOLD, CsaError, CsaProblem,
-    index_threshold_select, index_topk_decode, index_topk_interleaved, index_topk_prefill,
+    NOALLOC_SCRATCH_BYTES, OP_DECODE, OP_INTERLEAVED, OP_PREFILL, OP_RECALL, OP_THRESHOLD, CsaError, CsaProblem,
+    index_threshold_select, index_topk_decode, index_topk_decode_noalloc, index_topk_interleaved, index_topk_prefill,
     load_library, make_problem, set_recall, version, workspace_size,
     CsaAttnProblem, attention_workspace_size, make_attn_problem, sparse_attention, union_rows,
     MultiLayerSelector, MAX_LAYERS, batchable_layers, index_threshold_select_layers, MultiLayerIndexer,

@@ -59,6 +59,7 @@ _SIGS = {
     "csa_workspace_size": (_i32, [ctypes.c_int, _P, _i32, _i32, _u32, ctypes.POINTER(_sz)]),
     "csa_index_topk_prefill": (_i32, [_P, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_decode": (_i32, [_P, _i32, _u32, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_decode_noalloc": (_i32, [_P, _i32, _u32, _vp, _vp, _vp]),
     "csa_index_threshold_select": (_i32, [_P, _f32, _f32, _i32, _u32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_threshold_select_layers": (_i32, [ctypes.POINTER(_P), _i32, _f32, _f32, _i32, _u32,
                                                  ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
@@ -245,6 +246,25 @@ def index_topk_decode(q, k, w, topk, *, m=4, q_pos0=0, kv_len=None, sorted=False
     _check(load_library().csa_index_topk_decode(ctypes.byref(prob), int(topk), flags, _ptr(idx), _ptr(sc),
                                                 _ptr(ws), _nbytes(ws), _stream_handle()))
     return (idx, sc) if sc is not None else idx
+
+
+def index_topk_decode_noalloc(q, k, w, topk, *, m=4, q_pos0=0, kv_len=None, sorted=False, causal=True,
+                              return_scores=False, out=None, out_score=None):
+    """index_topk_decode that takes no workspace: the library uses its fixed
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES).  Calls that overlap on one GPU
+    race; calls on one stream are safe."""
+    torch = _torch()
+    prob = make_problem(q, k, w, m, q_pos0, kv_len)
+    B, S_q = q.shape[0], q.shape[1]
+    idx = out if out is not None else torch.empty((B, S_q, topk), dtype=torch.int32, device=q.device)
+    sc = out_score if out_score is not None else (
+        torch.empty((B, S_q, topk), dtype=torch.float32, device=q.device) if return_scores else None)
+    _check(load_library().csa_index_topk_decode_noalloc(ctypes.byref(prob), int(topk), _flags(sorted, causal),
+                                                        _ptr(idx), _ptr(sc), _stream_handle()))
+    return (idx, sc) if sc is not None else idx
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def index_threshold_select(q, k, w, cap, *, prob_threshold=0.5, logit_bias=0.0, m=4, q_pos0=0, kv_len=None,

@@ -383,6 +383,33 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
   }
 }
 
+csa_status csa_index_topk_decode_noalloc(const csa_problem* prob, int32_t topk, uint32_t flags, int32_t* out_idx,
+                                         float* out_score, void* hip_stream) {
+  try {
+    static_assert(CSA_NOALLOC_SCRATCH_BYTES == csa::NOALLOC_SCRATCH_BYTES, "scratch size");
+    csa_status s = validate_problem(prob);
+    if (s != CSA_OK) return s;
+    if ((s = validate_flags(flags)) != CSA_OK) return s;
+    if ((s = validate_k(topk, "topk")) != CSA_OK) return s;
+    if (!out_idx) return fail(CSA_ERR_INVALID, "out_idx is NULL");
+    if (prob->S_q > CSA_MAX_DECODE_SQ)
+      return fail(CSA_ERR_UNSUPPORTED, "decode needs S_q <= %d (got %d)", CSA_MAX_DECODE_SQ, prob->S_q);
+    if (!decode_fast(prob))
+      return fail(CSA_ERR_UNSUPPORTED, "the no-allocation decode needs bf16 q and k with H=64, D=128");
+    const DecodePlan d = plan_decode(prob, topk, flags);
+    if (d.total > csa::NOALLOC_SCRATCH_BYTES)
+      return fail(CSA_ERR_UNSUPPORTED, "problem needs %zu bytes of scratch, above the %zu this entry point holds "
+                  "(B*S_q*(T+64)*4 bytes of scores plus bounds); use csa_index_topk_decode with a workspace",
+                  d.total, csa::NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const hipError_t e = csa::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "scratch address lookup failed: %s", hipGetErrorString(e));
+    return run_decode(prob, topk, flags, 0ull, out_idx, out_score, nullptr, ws, csa::NOALLOC_SCRATCH_BYTES, hip_stream);
+  } catch (...) {
+    return fail(CSA_ERR_INVALID, "internal error");
+  }
+}
+
 csa_status csa_index_threshold_select(const csa_problem* prob, float prob_threshold, float logit_bias,
                                       int32_t cap, uint32_t flags, int32_t* out_idx, int32_t* out_count,
                                       float* out_score, void* ws, size_t ws_bytes, void* hip_stream) {

@@ -131,6 +131,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int mode, bool mfma, int grid, h
 // Resident workgroups per CU of the chosen prefill kernel (>= 1).
 int prefill_blocks_per_cu(int mode, bool mfma, bool bf16);
 hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st);
+
+// Scratch for the no-allocation decode entry point (csa_index_topk_decode_noalloc).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(8) << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+// This device's address of the scratch array (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_decode_batch(const DecodeBatch& bt, int nsplit, hipStream_t st);
 hipError_t launch_sort_rows(int32_t* idx, float* score, long long rows, int len, hipStream_t st);
 hipError_t launch_recall(const int32_t* sel, int n_sel, const int32_t* ref, int n_ref,

@@ -13,6 +13,8 @@
 //   the end the exact top-k of the buffer is emitted.
 // Decode: scores of a few queries against a long key range, split across
 //   many workgroups (HBM-bound), then one workgroup per row selects.
+#include <mutex>
+
 #include "csa_device.hpp"
 #include "csa_internal.hpp"
 
@@ -1555,6 +1557,31 @@ hipError_t launch_decode_batch(const DecodeBatch& bt, int nsplit, hipStream_t st
   if (e != hipSuccess) return e;
   decode_select_batch_kernel<<<dim3(a.B * a.S_q, 1, bt.L), DEC_SEL_THREADS, 0, st>>>(bt);
   return hipGetLastError();
+}
+
+// Fixed device scratch for csa_index_topk_decode_noalloc: callers that
+// cannot allocate get the decode workspace from this file-scope array (one
+// copy per GPU, held until the process ends).  Host code never uses the
+// array's name as an address: each device's address is asked once from the
+// runtime and kept.
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[NOALLOC_MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with this device current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int nsplit, hipStream_t st) {
