@@ -52,6 +52,7 @@ METRIC = "indexer TFLOP/s (% bf16 MFMA peak) prefill; decode key-scan GB/s (% HB
 HEADLINE_CFG = 5
 PAGES_MIN_RECALL_H200 = 0.9980       # StreamIndex abstract: min set-overlap recall, 1x H200 (context only)
 PAGES_PEAK_HBM_S1M_H200 = 6.21e9     # StreamIndex abstract: peak HBM at S = 1,048,576 on 1x H200 (context only)
+PREFILL_KERNEL = "prefill_mfma2_kernel<0>"  # the bf16 top-k prefill kernel the roofline is taken on
 
 
 def _log(msg):
@@ -600,9 +601,8 @@ def main():
     others = {}
     for cfg in [int(c) for c in args.prefill_configs.split(",") if c]:
         r = bench_prefill(args, torch, L, csa_inputs, R, cfg, max(args.steps, 20) if cfg == 2 else args.steps)
-        kname = "prefill_mfma_kernel<0>"
         d = prefill_summary(r, R)
-        tr = _traffic_record(kname, f"config {cfg}")
+        tr = _traffic_record(PREFILL_KERNEL, r["p"]["name"])
         d["traffic"] = None if tr is None else tr["hbm_bytes_per_launch"]
         others[str(cfg)] = d
     dec = None if args.no_decode else bench_decode(args, torch, L, csa_inputs, R)
@@ -615,10 +615,9 @@ def main():
     p = hl["p"]
     tflops = hl["flops"] / (hl["ms"] * 1e-3) / 1e12
     achieved = hl["flops"] / (hl["avg_ms"] * 1e-3) / 1e12
-    kname = "prefill_mfma_kernel<0>"
-    tr = _traffic_record(kname, f"config {HEADLINE_CFG}")
+    tr = _traffic_record(PREFILL_KERNEL, hl["p"]["name"])
     if dec is not None:
-        tr_d = _traffic_record("decode_score_kernel<2048>", "config 4")
+        tr_d = _traffic_record("decode_score_kernel<2048>", csa_inputs.config(4)["name"])
         dec["scan_traffic"] = None if tr_d is None else tr_d["hbm_bytes_per_launch"]
     line = {
         "metric": METRIC,
@@ -643,7 +642,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": kname,
+            "kernel": PREFILL_KERNEL,
             "achieved": round(achieved, 2),
             "peak": R.PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

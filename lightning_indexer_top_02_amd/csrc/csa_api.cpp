@@ -100,8 +100,26 @@ int cand_capacity(int kk) {
   return (int)((c + 63) / 64 * 64);
 }
 
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  return n;
+}
+
+int occupancy_cached(int mode, bool mfma, bool bf16) {
+  static std::mutex mu;
+  static int cache[64][3][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> g(mu);
+  int& c = cache[dev][mode][mfma][bf16];
+  if (c == 0) c = csa::prefill_blocks_per_cu(mode, mfma, bf16);
+  return c;
+}
+
 struct PrefillPlan {
-  int nqb, ws_slots, C;
+  int rows, nqb, ws_slots, C;
   long long n_items;
   size_t cand_bytes, sort_bytes, total;
 };
@@ -110,16 +128,21 @@ struct PrefillPlan {
 // kernels count rounds of the persistent grid in 32-bit ints.
 constexpr long long PF_MAX_ITEMS = (long long)INT_MAX - csa::PF_MAX_GRID;
 
-// Workspace layout: [ws_slots workgroups x PF_ROWS candidate buffers of C
-// keys][sort scratch when CSA_SORTED].
-PrefillPlan plan_prefill(const csa_problem* p, int kk, int P, int out_stride, uint32_t flags) {
+// Workspace layout: [ws_slots workgroups x rows-per-block candidate buffers of C
+// keys][sort scratch when CSA_SORTED].  ws_slots is the persistent grid: the
+// workgroups resident on this device at once (compute units x occupancy of
+// the chosen kernel), at most one per work item and at most PF_MAX_GRID.
+PrefillPlan plan_prefill(const csa_problem* p, int mode, int kk, int P, int out_stride, uint32_t flags) {
   PrefillPlan pl;
-  pl.nqb = (p->S_q + csa::PF_ROWS - 1) / csa::PF_ROWS;
+  const bool mfma = use_mfma(p);
+  pl.rows = csa::prefill_rows_per_block(mfma);
+  pl.nqb = (p->S_q + pl.rows - 1) / pl.rows;
   const long long items = (long long)p->B * pl.nqb * P;
   pl.n_items = items;
-  pl.ws_slots = (int)std::min<long long>(items, csa::PF_MAX_GRID);
+  const long long resident = (long long)device_cus() * occupancy_cached(mode, mfma, p->dtype == CSA_BF16);
+  pl.ws_slots = (int)std::min<long long>({items, std::max<long long>(1, resident), (long long)csa::PF_MAX_GRID});
   pl.C = cand_capacity(kk);
-  pl.cand_bytes = align_up((size_t)pl.ws_slots * csa::PF_ROWS * pl.C * sizeof(unsigned long long));
+  pl.cand_bytes = align_up((size_t)pl.ws_slots * pl.rows * pl.C * sizeof(unsigned long long));
   pl.sort_bytes = (flags & CSA_SORTED) ? align_up((size_t)p->B * p->S_q * out_stride * sizeof(float)) : 0;
   pl.total = pl.cand_bytes + pl.sort_bytes;
   return pl;
@@ -160,31 +183,13 @@ DecodePlan plan_decode(const csa_problem* p, int kk, uint32_t flags) {
   return d;
 }
 
-int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
-  return n;
-}
-
-int occupancy_cached(int mode, bool mfma, bool bf16) {
-  static std::mutex mu;
-  static int cache[64][3][2][2];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-  std::lock_guard<std::mutex> g(mu);
-  int& c = cache[dev][mode][mfma][bf16];
-  if (c == 0) c = csa::prefill_blocks_per_cu(mode, mfma, bf16);
-  return c;
-}
-
 csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uint32_t flags,
                               unsigned long long thr_fixed, int32_t* out_idx, float* out_score,
                               int32_t* out_count, void* ws, size_t ws_bytes, void* stream) {
   const int out_stride = kk * P;
-  const PrefillPlan pl = plan_prefill(p, kk, P, out_stride, flags);
+  const PrefillPlan pl = plan_prefill(p, mode, kk, P, out_stride, flags);
   if (pl.n_items > PF_MAX_ITEMS)
-    return fail(CSA_ERR_UNSUPPORTED, "B * ceil(S_q/%d) * P = %lld query blocks above %lld per call", csa::PF_ROWS,
+    return fail(CSA_ERR_UNSUPPORTED, "B * ceil(S_q/%d) * P = %lld query blocks above %lld per call", pl.rows,
                 pl.n_items, PF_MAX_ITEMS);
   const bool sorted = (flags & CSA_SORTED) != 0;
   const long long sort_rows = (long long)p->B * p->S_q * P;     // one sort workgroup per output row segment
@@ -212,8 +217,7 @@ csa_status run_prefill_family(const csa_problem* p, int mode, int kk, int P, uin
   a.need_scores = score_dst != nullptr;
   a.bf16 = p->dtype == CSA_BF16;
 
-  const int resident = device_cus() * occupancy_cached(mode, mfma, a.bf16);
-  const int grid = std::max(1, std::min(pl.ws_slots, resident));
+  const int grid = std::max(1, pl.ws_slots);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = csa::launch_prefill(a, mode, mfma, grid, st);
   if (e != hipSuccess) return fail(CSA_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
@@ -284,7 +288,10 @@ csa_status csa_workspace_size(int op, const csa_problem* prob, int32_t k_or_cap,
     if ((op == CSA_OP_DECODE || op == CSA_OP_THRESHOLD) && decode_fast(prob)) {
       *bytes = plan_decode(prob, k_or_cap, flags).total;
     } else {
-      *bytes = plan_prefill(prob, k_or_cap, parts, k_or_cap * parts, flags).total;
+      const int mode = op == CSA_OP_THRESHOLD     ? csa::MODE_THRESHOLD
+                       : op == CSA_OP_INTERLEAVED ? csa::MODE_INTERLEAVED
+                                                  : csa::MODE_TOPK;
+      *bytes = plan_prefill(prob, mode, k_or_cap, parts, k_or_cap * parts, flags).total;
     }
     return ok();
   } catch (...) {

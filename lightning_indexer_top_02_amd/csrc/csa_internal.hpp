@@ -17,6 +17,14 @@ constexpr int PF_THREADS = 256;
 constexpr int PF_MAX_GRID = 512;
 // Keys per LDS stage of the MFMA prefill kernel.
 constexpr int PF_KTILE = 64;
+// The MFMA prefill kernel (bf16, H = 64, D = 128): 8 waves x 1 query row per
+// workgroup in two groups half a step apart, one workgroup per CU, a ring of
+// three key-tile stages in LDS.
+constexpr int PF2_ROWS = 8;
+constexpr int PF2_THREADS = 512;
+constexpr int PF2_NSTAGE = 3;
+// Query rows per workgroup item of the chosen prefill kernel.
+constexpr int prefill_rows_per_block(bool mfma) { return mfma ? PF2_ROWS : PF_ROWS; }
 
 struct PrefillArgs {
   const void* q;
@@ -28,14 +36,14 @@ struct PrefillArgs {
   int causal;
   int kk;               // topk / cap / k_local
   int P;                // partitions (1 unless interleaved)
-  int nqb;              // query blocks per (b): ceil(S_q / PF_ROWS)
+  int nqb;              // query blocks per (b): ceil(S_q / rows per block)
   int n_items;          // B * nqb * P
   unsigned long long thr_fixed;  // threshold mode: smallest surviving key
   int32_t* out_idx;
   float* out_score;     // may be null
   int32_t* out_count;   // threshold mode
   int out_stride;       // entries per output row (kk, or P*kk when interleaved)
-  unsigned long long* cand;      // [grid][PF_ROWS][C] candidate buffers, one per wave
+  unsigned long long* cand;      // [grid][rows per block][C] candidate buffers, one per query row
   int C;                // candidate capacity per query row, >= kk + 64
   int need_scores;      // out_score != null
   int bf16;             // element type of q and k: 1 = bf16, 0 = fp32

@@ -5,9 +5,10 @@
 // per-query running top-k; the [B,S,H,T] score tensor is never formed.
 //
 // Prefill family (top-k, threshold, interleaved partitions):
-//   persistent grid; a workgroup owns PF_ROWS = 4 consecutive query rows,
-//   one per wave.  Per step the wave produces 64 (query, key) scores, one per
-//   lane, filters them against the query's running threshold key and appends
+//   persistent grid; a workgroup owns consecutive query rows, one per wave
+//   (8 in the MFMA kernel, 4 in the generic one).  Per step the wave produces
+//   64 (query, key) scores, one per lane, filters them against the query's
+//   running threshold key and appends
 //   survivors to the query's candidate buffer in the workspace.  A full
 //   buffer is compacted to the exact top-k (which raises the threshold); at
 //   the end the exact top-k of the buffer is emitted.
@@ -287,12 +288,12 @@ __device__ __forceinline__ int round_item(int r) {
 
 // Does any row of the block need scores (more visible keys than kk, scores
 // requested, or threshold mode)?  Also the block's largest visible count.
-template <int MODE>
+template <int MODE, int ROWS = PF_ROWS>
 __device__ __forceinline__ bool block_needs_scores(const PrefillArgs& a, int b, int qb, int part, int& vis_max) {
   vis_max = 0;
   bool need = MODE == MODE_THRESHOLD || a.need_scores;
-  for (int r = 0; r < PF_ROWS; ++r) {
-    const int v = row_visible(a, b, qb * PF_ROWS + r, part);
+  for (int r = 0; r < ROWS; ++r) {
+    const int v = row_visible(a, b, qb * ROWS + r, part);
     vis_max = v > vis_max ? v : vis_max;
     need = need || v > a.kk;
   }
@@ -365,10 +366,9 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 // Output lane l holds key column (l & 31) and 16 heads of a row tile; ReLU and
 // the head weights are applied in registers; exchanging the two column tiles'
 // half-wave partial sums leaves lanes 0-31 with the scores of tile 0 and lanes
-// 32-63 with those of tile 1.  Two workgroups share a CU (two waves per SIMD),
-// so one wave's VALU epilogue overlaps the other's MFMAs.  Each wave filters
-// its row's scores into a candidate list (compacted to the top-kk when full)
-// and selects the row's final top-kk from it at the end of the query block.
+// 32-63 with those of tile 1.  Each wave filters its row's scores into a
+// candidate list (compacted to the top-kk when full) and selects the row's
+// final top-kk from it at the end of the query block.
 
 constexpr int MH = 64, MD = 128;
 // A key tile (PF_KTILE keys x 256 B) sits in LDS as groups of 16 keys; inside
@@ -380,25 +380,42 @@ constexpr int MH = 64, MD = 128;
 // lanes, with the k-step in the instruction's immediate offset.
 constexpr int KT_BYTES = PF_KTILE * MD * 2;
 
+// ============================================================ MFMA prefill, ping-pong
+//
+// The same computation with eight waves (one query row each) per workgroup
+// and one workgroup per CU, so every SIMD runs two waves of one workgroup:
+// wave w and wave w + 4.  A SIMD overlaps one wave's MFMAs with another
+// wave's VALU work, but not with its own, and waves that run the same phase
+// at the same time only compete.  So the two groups of four waves run half a
+// step apart: each step of a wave is an MFMA half (B operands from LDS, 32
+// MFMAs) and a VALU half (ReLU, head weights, offer, key-tile requests), and
+// workgroup barriers between the halves keep group 1's MFMA half under group
+// 0's VALU half and the other way round.  Each key tile in LDS serves eight
+// rows.  A ring of PF2_NSTAGE = 3 tiles: the tile two steps ahead is
+// requested in a VALU half, after every reader of the stage it overwrites has
+// passed a barrier, and each wave waits for its own requests at the end of
+// its next MFMA half, before the barrier after which the tile is read.  The
+// arithmetic and its order are those of the other kernels (bitwise the same
+// scores).
 template <int MODE>
-__global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char ktile[2][KT_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t hist_all[PF_THREADS / WAVE][SEL_BINS];
-  __shared__ u64 list_all[PF_THREADS / WAVE][WAVE_LIST];
+__global__ __launch_bounds__(PF2_THREADS, 1) void prefill_mfma2_kernel(PrefillArgs a) {
+  constexpr int NW = PF2_THREADS / WAVE;           // 8 waves
+  constexpr int NB = 16 / NW;                       // 1 KB tile blocks requested per wave
+  __shared__ __attribute__((aligned(1024))) char ktile[PF2_NSTAGE][KT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[NW][SEL_BINS];
+  __shared__ u64 list_all[NW][WAVE_LIST];
 
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  const int grp = wv / 4;                           // group 0: waves 0-3, group 1: waves 4-7
   uint32_t* hist = hist_all[wv];
   u64* list = list_all[wv];
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
-  // B-operand read offset of this lane inside a stage (column tile 0, k-step 0)
   const int b_off = ((l >> 4) & 1) * 4096 + (l >> 5) * 256 + (l & 15) * 16;
-  // byte offsets of this lane's 16-B pieces in the wave's four stage blocks,
-  // relative to the tile's first key row (rows are P keys apart)
-  uint32_t doff[4];
+  uint32_t doff[NB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int blk = e * 4 + wv, row = (blk >> 2) * 16 + (l & 15), chunk = (blk & 3) * 4 + (l >> 4);
+  for (int e = 0; e < NB; ++e) {
+    const int blk = e * NW + wv, row = (blk >> 2) * 16 + (l & 15), chunk = (blk & 3) * 4 + (l >> 4);
     doff[e] = (uint32_t)(((size_t)row * a.P * MD + chunk * 8) * 2);
   }
 
@@ -409,8 +426,8 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
     int b, qb, part;
     decode_item(a, it, b, qb, part);
     int vis_max;
-    const bool need = block_needs_scores<MODE>(a, b, qb, part, vis_max);
-    const int row = qb * PF_ROWS + wv;                // this wave's query row
+    const bool need = block_needs_scores<MODE, PF2_ROWS>(a, b, qb, part, vis_max);   // uniform
+    const int row = qb * PF2_ROWS + wv;               // this wave's query row
     const int vis = row_visible(a, b, row, part);
     if (!need) {
       if (row < a.S_q) wave_emit_all_visible(a, b, row, part, vis);
@@ -430,62 +447,44 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
       for (int i = 0; i < 16; ++i) wl[rt][i] = wrow[8 * (i >> 2) + (i & 3)];
     }
     Slot st;
-    slot_init(st, a.cand + ((size_t)blockIdx.x * PF_ROWS + wv) * a.C, a, MODE);
+    slot_init(st, a.cand + ((size_t)blockIdx.x * PF2_ROWS + wv) * a.C, a, MODE);
 
     const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
     const size_t kseq = (size_t)b * a.T;
-    // direct-to-LDS stage load: this wave fills blocks wv, wv+4, wv+8, wv+12 (1 KB
-    // each); a tile whose 64 rows all lie below T takes one uniform base plus the
-    // wave's constant lane offsets, a tile crossing T clamps its rows.
+    // this wave's share of tile t (blocks wv and wv + 8, 1 KB each) into stage buf
     auto load_tile = [&](int t, int buf) {
-      const size_t row0 = kseq + (size_t)part + (size_t)a.P * (size_t)(t * PF_KTILE);
+      const size_t krow0 = kseq + (size_t)part + (size_t)a.P * (size_t)(t * PF_KTILE);
       if ((long long)part + (long long)a.P * (t * PF_KTILE + PF_KTILE - 1) < a.T) {
-        const char* base = (const char*)(K + row0 * MD);
+        const char* base = (const char*)(K + krow0 * MD);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dma16(base + doff[e], lds_addr(&ktile[buf][(e * 4 + wv) * 1024]));
+        for (int e = 0; e < NB; ++e) dma16(base + doff[e], lds_addr(&ktile[buf][(e * NW + wv) * 1024]));
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int blk = e * 4 + wv, grp = blk >> 2, quad = blk & 3;
-          int j = t * PF_KTILE + grp * 16 + (l & 15);
+        for (int e = 0; e < NB; ++e) {
+          const int blk = e * NW + wv, gk = blk >> 2, quad = blk & 3;
+          int j = t * PF_KTILE + gk * 16 + (l & 15);
           j = j < vis_max ? j : vis_max - 1;          // rows past the end: any valid row (masked later)
           const int chunk = quad * 4 + (l >> 4);
-          const __bf16* src = K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8;
-          dma16(src, lds_addr(&ktile[buf][blk * 1024]));
+          dma16(K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8, lds_addr(&ktile[buf][blk * 1024]));
         }
       }
     };
     __syncthreads();                                  // previous item's readers are done with the stages
-    if (ntiles > 0) load_tile(0, 0);
-    // tile 0 and the query loads have landed; the compiler, which does not see
-    // the tile loads, then has no load of its own pending inside the loop
+#pragma unroll
+    for (int s0 = 0; s0 < PF2_NSTAGE - 1; ++s0)
+      if (s0 < ntiles) load_tile(s0, s0);
     wait_vmcnt<0>();
     __syncthreads();
+    if (grp == 1) __syncthreads();                    // group 1 runs half a step behind group 0
 
-    // Step t covers keys [64t, 64t+64): column tile 0 = keys 64t + (l & 31),
-    // column tile 1 = keys 64t + 32 + (l & 31).  The scores of tile t are
-    // offered at the start of step t+1 (the offer's global stores then have a
-    // whole step to complete before the vmcnt wait at its end).  Tile t+1 is
-    // requested after step t's MFMAs, while the wave reduces their results:
-    // its bytes then land in LDS during the VALU work instead of competing
-    // with the MFMA operand reads (measured 32.5 -> 30.9 ms on the million-token
-    // tail; the wait at the end of the step stays covered).
-    float pend = 0.f;
-    auto flush = [&](int t) {
-      const int j = t * PF_KTILE + l;
-      wave_offer<MODE>(st, pend, (uint32_t)(part + a.P * j), j < vis, a, hist, list);
-    };
     for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t > 0) flush(t - 1);
-      const char* kb = &ktile[buf][b_off];
+      // ---- MFMA half: step t's key tile from stage t % PF2_NSTAGE
+      const char* kb = &ktile[t % PF2_NSTAGE][b_off];
       f32x16 acc[2][2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) acc[c][rt] = f32x16{};
-      // B operands one k-step ahead; the scheduling fences keep the compiler
-      // from hoisting all 16 LDS reads (64 VGPRs) to the top of the step.
       bf16x8 b0 = *(const bf16x8*)(kb);
       bf16x8 b1 = *(const bf16x8*)(kb + 8192);
 #pragma unroll
@@ -504,7 +503,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
         b0 = n0;
         b1 = n1;
       }
-      if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);   // stage t+1 was last read in step t-1
+      wait_vmcnt<0>();                                 // this wave's requests of the last VALU half landed
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);               // the VALU half stays after the barrier
+      // ---- VALU half: reduce step t, offer it, request the tile two steps ahead
       float part2[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -515,11 +517,17 @@ __global__ __launch_bounds__(PF_THREADS, 2) void prefill_mfma_kernel(PrefillArgs
           for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[c][rt][i]), ps);
         part2[c] = ps;
       }
-      pend = half_swap_sum(part2[0], part2[1]);
-      wait_vmcnt<0>();                                 // this wave's part of tile t+1 landed
-      __syncthreads();                                 // all of tile t+1 landed and stage t is free
+      {
+        const int j = t * PF_KTILE + l;
+        wave_offer<MODE>(st, half_swap_sum(part2[0], part2[1]), (uint32_t)(part + a.P * j), j < vis, a, hist,
+                         list);
+      }
+      // stage (t + 2) % 3 last held step t - 1, whose readers passed a barrier before this half began
+      if (t + PF2_NSTAGE - 1 < ntiles) load_tile(t + PF2_NSTAGE - 1, (t + PF2_NSTAGE - 1) % PF2_NSTAGE);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);               // the next MFMA half stays after the barrier
     }
-    if (ntiles > 0) flush(ntiles - 1);
+    if (grp == 0) __syncthreads();                    // both groups pass the same number of barriers
     finish_row<MODE>(a, st, b, row, part, hist, list);
   }
 }
@@ -1508,7 +1516,7 @@ __global__ __launch_bounds__(RECALL_THREADS) void recall_kernel(const int32_t* s
 
 template <int MODE>
 static const void* prefill_kernel_ptr(bool mfma, bool bf16) {
-  if (mfma) return (const void*)prefill_mfma_kernel<MODE>;
+  if (mfma) return (const void*)prefill_mfma2_kernel<MODE>;
   if (bf16) return (const void*)prefill_generic_kernel<MODE, __bf16>;
   return (const void*)prefill_generic_kernel<MODE, float>;
 }
@@ -1521,18 +1529,20 @@ static const void* prefill_kernel_for(int mode, bool mfma, bool bf16) {
   }
 }
 
-static int blocks_per_cu(const void* fn) {
+static int blocks_per_cu(const void* fn, int threads) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, PF_THREADS, 0) != hipSuccess || n < 1) n = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 1) n = 1;
   return n;
 }
 
-int prefill_blocks_per_cu(int mode, bool mfma, bool bf16) { return blocks_per_cu(prefill_kernel_for(mode, mfma, bf16)); }
+int prefill_blocks_per_cu(int mode, bool mfma, bool bf16) {
+  return blocks_per_cu(prefill_kernel_for(mode, mfma, bf16), mfma ? PF2_THREADS : PF_THREADS);
+}
 
 template <int MODE>
 static void launch_prefill_mode(const PrefillArgs& a, bool mfma, int grid, hipStream_t st) {
   if (mfma)
-    prefill_mfma_kernel<MODE><<<grid, PF_THREADS, 0, st>>>(a);
+    prefill_mfma2_kernel<MODE><<<grid, PF2_THREADS, 0, st>>>(a);
   else if (a.bf16)
     prefill_generic_kernel<MODE, __bf16><<<grid, PF_THREADS, 0, st>>>(a);
   else
