@@ -43,7 +43,8 @@ __device__ __forceinline__ float key_score(u64 key) { return order_bits_score((u
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ u64 ballot(bool p) { return __ballot(p); }
+// (the i1 form: no round trip of the predicate through a VGPR)
+__device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(u64 mask) {

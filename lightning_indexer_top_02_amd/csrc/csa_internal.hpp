@@ -19,10 +19,10 @@ constexpr int PF_MAX_GRID = 512;
 constexpr int PF_KTILE = 64;
 // The MFMA prefill kernel (bf16, H = 64, D = 128): 8 waves x 1 query row per
 // workgroup in two groups half a step apart, one workgroup per CU, a ring of
-// three key-tile stages in LDS.
+// four key-tile stages in LDS.
 constexpr int PF2_ROWS = 8;
 constexpr int PF2_THREADS = 512;
-constexpr int PF2_NSTAGE = 3;
+constexpr int PF2_NSTAGE = 4;
 // Query rows per workgroup item of the chosen prefill kernel.
 constexpr int prefill_rows_per_block(bool mfma) { return mfma ? PF2_ROWS : PF_ROWS; }
 

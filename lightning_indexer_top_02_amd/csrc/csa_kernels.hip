@@ -357,6 +357,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (the instruction's saddr form): the per-step address update is
+// scalar work only.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m)
+               : "memory", "m0");
+}
+
 // ============================================================ MFMA prefill
 //
 // bf16, H = 64 heads, D = 128.  A wave holds its query's 64 heads x 128 as
@@ -382,7 +391,7 @@ constexpr int KT_BYTES = PF_KTILE * MD * 2;
 
 // ============================================================ MFMA prefill, ping-pong
 //
-// The same computation with eight waves (one query row each) per workgroup
+// The computation above with eight waves (one query row each) per workgroup
 // and one workgroup per CU, so every SIMD runs two waves of one workgroup:
 // wave w and wave w + 4.  A SIMD overlaps one wave's MFMAs with another
 // wave's VALU work, but not with its own, and waves that run the same phase
@@ -391,33 +400,94 @@ constexpr int KT_BYTES = PF_KTILE * MD * 2;
 // MFMAs) and a VALU half (ReLU, head weights, offer, key-tile requests), and
 // workgroup barriers between the halves keep group 1's MFMA half under group
 // 0's VALU half and the other way round.  Each key tile in LDS serves eight
-// rows.  A ring of PF2_NSTAGE = 3 tiles: the tile two steps ahead is
-// requested in a VALU half, after every reader of the stage it overwrites has
-// passed a barrier, and each wave waits for its own requests at the end of
-// its next MFMA half, before the barrier after which the tile is read.  The
-// arithmetic and its order are those of the other kernels (bitwise the same
-// scores).
+// rows.  A ring of PF2_NSTAGE = 4 tiles: the tile three steps ahead is
+// requested in a VALU half, after every reader of the stage it overwrites
+// (step t - 1, both groups) has passed a barrier, and each wave waits for its
+// own requests of tile t + 1 at the end of its MFMA half t, before the
+// barrier after which either group reads that tile.  The VALU half is kept
+// short, since it is the longer of the two: scores become 64-bit keys at
+// once and the running threshold is a key, the candidate stores and the
+// key-tile requests take wave-uniform bases in SGPRs with 32-bit lane
+// offsets.  The arithmetic and its order are those of the other kernels
+// (bitwise the same scores).
+// Running top-k state of one wave's query row in the MFMA kernel, kept in
+// key form: a key (order bits of the score, ~index) may enter iff key >= X,
+// the same total order as Slot's (score, index) threshold.  lo_o / hi_o (per
+// lane) are the order bits of the smallest and largest score this lane
+// appended (unsigned min / max of order bits = min / max of the scores).
+struct KeySlot {
+  u64* cand;
+  int cnt;
+  u64 X;
+  int surv;
+  uint32_t lo_o, hi_o;
+};
+
+// The compaction of a full candidate buffer, out of line: it runs a few
+// times per query row, and inlined its scalar temporaries would crowd the
+// MFMA kernel's tile loop into spilling SGPRs.
+__device__ __attribute__((noinline)) u64 wave_compact_call(u64* buf, int cnt, int kk, uint32_t* hist, u64* list,
+                                                           float lo, float hi) {
+  return wave_compact(buf, cnt, kk, hist, list, lo, hi);
+}
+
+// Offer one key per lane (valid lanes only) to the wave's query row.
+template <int MODE>
+__device__ __forceinline__ void key_offer(KeySlot& st, u64 key, bool valid, const PrefillArgs& a, uint32_t* hist,
+                                          u64* list) {
+  if (st.cnt + WAVE > a.C) {                          // make room: at most 64 appends per offer
+    const u64 T = wave_compact_call(st.cand, st.cnt, a.kk, hist, list, order_bits_score(st.lo_o),
+                                    order_bits_score(st.hi_o));
+    st.cnt = a.kk;
+    st.lo_o = (uint32_t)(T >> 32);                    // every survivor scores >= the kk-th
+    st.X = (MODE == MODE_THRESHOLD && a.thr_fixed > T + 1ull) ? a.thr_fixed : T + 1ull;
+  }
+  if (MODE == MODE_THRESHOLD) st.surv += __popcll(ballot(valid && key >= a.thr_fixed));
+  const bool keep = valid && key >= st.X;
+  const u64 m = ballot(keep);
+  if (keep) {
+    const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)st.cnt));
+    __builtin_nontemporal_store(key, (u64*)((char*)st.cand + pos * 8u));
+    const uint32_t o = (uint32_t)(key >> 32);
+    st.lo_o = o < st.lo_o ? o : st.lo_o;
+    st.hi_o = o > st.hi_o ? o : st.hi_o;
+  }
+  st.cnt += __popcll(m);
+}
+
+// Order bits of a score that is never -0.0 (see the kernel): no -0.0 fold.
+__device__ __forceinline__ uint32_t order_bits_nz(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 template <int MODE>
 __global__ __launch_bounds__(PF2_THREADS, 1) void prefill_mfma2_kernel(PrefillArgs a) {
   constexpr int NW = PF2_THREADS / WAVE;           // 8 waves
   constexpr int NB = 16 / NW;                       // 1 KB tile blocks requested per wave
+  static_assert((PF2_NSTAGE & (PF2_NSTAGE - 1)) == 0 && PF2_NSTAGE >= 4, "ring of 2^n >= 4 stages");
   __shared__ __attribute__((aligned(1024))) char ktile[PF2_NSTAGE][KT_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t hist_all[NW][SEL_BINS];
   __shared__ u64 list_all[NW][WAVE_LIST];
 
-  const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
+  const int tid = threadIdx.x, l = tid & (WAVE - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / WAVE);   // wave-uniform: scalar address math
   const int grp = wv / 4;                           // group 0: waves 0-3, group 1: waves 4-7
   uint32_t* hist = hist_all[wv];
   u64* list = list_all[wv];
   const __bf16* Q = (const __bf16*)a.q;
   const __bf16* K = (const __bf16*)a.k;
   const int b_off = ((l >> 4) & 1) * 4096 + (l >> 5) * 256 + (l & 15) * 16;
-  uint32_t doff[NB];
+  uint32_t doff[NB], dlds[NB];
 #pragma unroll
   for (int e = 0; e < NB; ++e) {
     const int blk = e * NW + wv, row = (blk >> 2) * 16 + (l & 15), chunk = (blk & 3) * 4 + (l >> 4);
     doff[e] = (uint32_t)(((size_t)row * a.P * MD + chunk * 8) * 2);
+    dlds[e] = lds_addr(&ktile[0][blk * 1024]);
   }
+  const uint32_t tile_step = (uint32_t)a.P * PF_KTILE;        // key rows per tile
+  const size_t tile_bytes = (size_t)tile_step * MD * 2;
 
   for (int r = 0;; ++r) {
     const int it = round_item(r);
@@ -446,18 +516,27 @@ __global__ __launch_bounds__(PF2_THREADS, 1) void prefill_mfma2_kernel(PrefillAr
 #pragma unroll
       for (int i = 0; i < 16; ++i) wl[rt][i] = wrow[8 * (i >> 2) + (i & 3)];
     }
-    Slot st;
-    slot_init(st, a.cand + ((size_t)blockIdx.x * PF2_ROWS + wv) * a.C, a, MODE);
+    KeySlot st;
+    st.cand = a.cand + ((size_t)blockIdx.x * PF2_ROWS + wv) * a.C;
+    st.cnt = 0;
+    st.X = MODE == MODE_THRESHOLD ? a.thr_fixed : 0ull;
+    st.surv = 0;
+    st.lo_o = 0xFF800000u;                            // order bits of +inf
+    st.hi_o = 0x007FFFFFu;                            // order bits of -inf
+    // ~index of this lane's key in step t: nidx0 - t * tile_step
+    const uint32_t nidx0 = 0xFFFFFFFFu - (uint32_t)(part + a.P * l);
 
     const int ntiles = (vis_max + PF_KTILE - 1) / PF_KTILE;
     const size_t kseq = (size_t)b * a.T;
+    const char* kbase = (const char*)(K + (kseq + (size_t)part) * MD);
+    // tiles 0 .. nfull-1 hold PF_KTILE keys below T: part + P (64 t + 63) < T
+    const long long lim = (long long)a.T - 1 - part - (long long)(PF_KTILE - 1) * a.P;
+    const int nfull = lim < 0 ? 0 : (int)(lim / tile_step + 1 < ntiles ? lim / tile_step + 1 : ntiles);
     // this wave's share of tile t (blocks wv and wv + 8, 1 KB each) into stage buf
-    auto load_tile = [&](int t, int buf) {
-      const size_t krow0 = kseq + (size_t)part + (size_t)a.P * (size_t)(t * PF_KTILE);
-      if ((long long)part + (long long)a.P * (t * PF_KTILE + PF_KTILE - 1) < a.T) {
-        const char* base = (const char*)(K + krow0 * MD);
+    auto load_tile = [&](int t, int buf, const char* base) {
+      if (t < nfull) {
 #pragma unroll
-        for (int e = 0; e < NB; ++e) dma16(base + doff[e], lds_addr(&ktile[buf][(e * NW + wv) * 1024]));
+        for (int e = 0; e < NB; ++e) dma16s(base, doff[e], dlds[e] + (uint32_t)buf * KT_BYTES);
       } else {
 #pragma unroll
         for (int e = 0; e < NB; ++e) {
@@ -465,28 +544,33 @@ __global__ __launch_bounds__(PF2_THREADS, 1) void prefill_mfma2_kernel(PrefillAr
           int j = t * PF_KTILE + gk * 16 + (l & 15);
           j = j < vis_max ? j : vis_max - 1;          // rows past the end: any valid row (masked later)
           const int chunk = quad * 4 + (l >> 4);
-          dma16(K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8, lds_addr(&ktile[buf][blk * 1024]));
+          dma16(K + (kseq + (size_t)part + (size_t)a.P * j) * MD + chunk * 8, dlds[e] + (uint32_t)buf * KT_BYTES);
         }
       }
     };
     __syncthreads();                                  // previous item's readers are done with the stages
+    const int t_part = grp == 0 ? ntiles - 2 : -1;    // steps whose MFMA half ends with a partial wait
+    const char* knext = kbase;                        // global address of the next tile to request
 #pragma unroll
-    for (int s0 = 0; s0 < PF2_NSTAGE - 1; ++s0)
-      if (s0 < ntiles) load_tile(s0, s0);
+    for (int s0 = 0; s0 < PF2_NSTAGE - 1; ++s0) {
+      if (s0 < ntiles) load_tile(s0, s0, knext);
+      knext += tile_bytes;
+    }
     wait_vmcnt<0>();
     __syncthreads();
+    // first B operands of step 0 (each MFMA half starts with its first B operands in registers)
+    bf16x8 b0 = *(const bf16x8*)(&ktile[0][b_off]);
+    bf16x8 b1 = *(const bf16x8*)(&ktile[0][b_off + 8192]);
     if (grp == 1) __syncthreads();                    // group 1 runs half a step behind group 0
 
     for (int t = 0; t < ntiles; ++t) {
       // ---- MFMA half: step t's key tile from stage t % PF2_NSTAGE
-      const char* kb = &ktile[t % PF2_NSTAGE][b_off];
+      const char* kb = &ktile[t & (PF2_NSTAGE - 1)][b_off];
       f32x16 acc[2][2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) acc[c][rt] = f32x16{};
-      bf16x8 b0 = *(const bf16x8*)(kb);
-      bf16x8 b1 = *(const bf16x8*)(kb + 8192);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         bf16x8 n0 = b0, n1 = b1;
@@ -503,10 +587,15 @@ __global__ __launch_bounds__(PF2_THREADS, 1) void prefill_mfma2_kernel(PrefillAr
         b0 = n0;
         b1 = n1;
       }
-      wait_vmcnt<0>();                                 // this wave's requests of the last VALU half landed
+      // Group 0: this wave's share of tile t + 1 landed (its requests for
+      // t + 2, the last vector-memory instructions it issued, may still fly).
+      // Group 1: its share of tile t + 2 landed as well, before the barrier
+      // that ends group 0's MFMA half t + 1: group 0 reads tile t + 2's first
+      // B operands at the end of its VALU half t + 1.
+      if (t < t_part) wait_vmcnt<NB>(); else wait_vmcnt<0>();
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);               // the VALU half stays after the barrier
-      // ---- VALU half: reduce step t, offer it, request the tile two steps ahead
+      // ---- VALU half: reduce step t, offer it, request the tile three steps ahead
       float part2[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -517,18 +606,34 @@ __global__ __launch_bounds__(PF2_THREADS, 1) void prefill_mfma2_kernel(PrefillAr
           for (int i = 0; i < 16; ++i) ps = __builtin_fmaf(wl[rt][i], relu(acc[c][rt][i]), ps);
         part2[c] = ps;
       }
-      {
-        const int j = t * PF_KTILE + l;
-        wave_offer<MODE>(st, half_swap_sum(part2[0], part2[1]), (uint32_t)(part + a.P * j), j < vis, a, hist,
-                         list);
+      // The score is never -0.0: each partial sum starts as fma(w, r, +0) with
+      // r >= +0, so it is +0 or non-zero, and later fmas and the final add
+      // return -0.0 only from two -0.0 operands.
+      // The next MFMA half's first B operands, read here so that the offer
+      // hides their latency: tile t + 1 is whole in LDS (both groups' shares
+      // landed before the barrier that began this half).
+      if (t + 1 < ntiles) {
+        const char* kn = &ktile[(t + 1) & (PF2_NSTAGE - 1)][b_off];
+        b0 = *(const bf16x8*)(kn);
+        b1 = *(const bf16x8*)(kn + 8192);
       }
-      // stage (t + 2) % 3 last held step t - 1, whose readers passed a barrier before this half began
-      if (t + PF2_NSTAGE - 1 < ntiles) load_tile(t + PF2_NSTAGE - 1, (t + PF2_NSTAGE - 1) % PF2_NSTAGE);
+      const float score = half_swap_sum(part2[0], part2[1]);
+      const u64 key = ((u64)order_bits_nz(score) << 32) | (u64)(nidx0 - (uint32_t)t * tile_step);
+      key_offer<MODE>(st, key, l < vis - t * PF_KTILE, a, hist, list);
+      // stage (t + 3) % 4 last held step t - 1, whose readers passed a barrier before this half began
+      if (t + PF2_NSTAGE - 1 < ntiles) load_tile(t + PF2_NSTAGE - 1, (t + PF2_NSTAGE - 1) & (PF2_NSTAGE - 1), knext);
+      knext += tile_bytes;
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);               // the next MFMA half stays after the barrier
     }
     if (grp == 0) __syncthreads();                    // both groups pass the same number of barriers
-    finish_row<MODE>(a, st, b, row, part, hist, list);
+    Slot fs;
+    fs.cand = st.cand;
+    fs.cnt = st.cnt;
+    fs.surv = st.surv;
+    fs.lo = order_bits_score(st.lo_o);
+    fs.hi = order_bits_score(st.hi_o);
+    finish_row<MODE>(a, fs, b, row, part, hist, list);
   }
 }
 
