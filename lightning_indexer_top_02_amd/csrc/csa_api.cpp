@@ -84,17 +84,18 @@ bool use_mfma(const csa_problem* p) {
   return p->dtype == CSA_BF16 && p->H == 64 && p->D == 128;
 }
 
-// Candidate buffer capacity per query row: the top-k plus three times as many
-// appends between compactions (4k + 64).  The minimum that keeps progress is
-// 2k + 64 (every compaction select then fits the registers for k <= 2048),
-// but long rows compact less often with the larger buffer and run faster
-// (S=65536, T=16384, k=2048: 11.1 -> 10.3 ms), while rows of at most 4k
-// visible keys never compact at either size.  The CSA_OPT_CAND_CAP test
-// option overrides it (tests force frequent compactions); it is clamped to
-// the minimum.
+// Candidate buffer capacity per query row: the top-k plus eleven times as
+// many appends between compactions (12k + 64).  The minimum that keeps
+// progress is 2k + 64, but every compaction holds the MFMA kernel's whole
+// workgroup at a barrier, so long rows run faster with fewer, larger ones
+// (k = 2048, measured against 4k + 64: the million-token tail 27.6 -> 26.9
+// ms, S=65536/T=16384 8.78 -> 8.49 ms; 16k + 64 and more are slower again, as
+// the first fill offers every key).  Rows of at most 12k visible keys never
+// compact.  The CSA_OPT_CAND_CAP test option overrides it (tests force
+// frequent compactions); it is clamped to the minimum.
 int cand_capacity(int kk) {
   const int lo = 2 * kk + 64;
-  long long c = 4ll * kk + 64;
+  long long c = 12ll * kk + 64;
   const long long v = g_opt_cand_cap.load(std::memory_order_relaxed);
   if (v > 0) c = std::max<long long>(v, lo);
   return (int)((c + 63) / 64 * 64);
