@@ -111,11 +111,11 @@ def _time_calls(torch, call, steps, warmup, min_warm_ms):
 
 
 def kernel_source_sha256():
-    """sha256 over the device sources (kernels and the headers they include),
-    in a fixed order: a traffic record applies only to the source it was
-    measured on."""
+    """sha256 over the device sources (kernels and the headers they include)
+    and the host code that sizes their launches and workspaces, in a fixed
+    order: a traffic record applies only to the source it was measured on."""
     h = hashlib.sha256()
-    for f in ("csa_kernels.hip", "csa_device.hpp", "csa_internal.hpp"):
+    for f in ("csa_kernels.hip", "csa_device.hpp", "csa_internal.hpp", "csa_api.cpp"):
         h.update(open(os.path.join(ROOT, "lightning_indexer_top_02_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
