@@ -83,10 +83,67 @@ __device__ __forceinline__ bool passes(float s, uint32_t i, float ts, uint32_t t
   return s > ts || (s == ts && i <= ti);
 }
 
+// Exact top-kk of buf[0..n) (n > kk) in two streaming passes: a linear-bin
+// histogram between the lanes' score bounds lo / hi, then one pass that hands
+// every key of a bin above the bin holding rank kk to put(key, position)
+// (positions 0, 1, ... in buffer order) and gathers that bin's keys into the
+// LDS list, whose exact rank-r key T is found there; the list's keys >= T
+// follow (positions up to kk - 1).  Returns T, or 0 when the bins cannot
+// narrow the rank (no usable range, or a bin too crowded for the list): the
+// caller then takes the general selection and nothing has been put.  put
+// may write back into buf: a key goes to a position at or below the one it
+// was read from.
+template <typename Put>
+__device__ __forceinline__ u64 wave_binned_select(const u64* buf, int n, int kk, uint32_t* hist, u64* list,
+                                                  float lo, float hi, Put put) {
+  const int l = lane_id();
+  LinBins lb;
+  if (!lin_bins_ok(lo, hi, lb)) return 0ull;
+  wave_clear_hist(hist, SEL_BINS);
+  wave_lds_sync();
+  wave_stream(buf, n, [&](u64 v, int) {
+    if (v) atomicAdd(&hist[lb(v)], 1u);
+  });
+  wave_lds_sync();
+  const BinPick pk = wave_pick_bin(hist, SEL_BINS, kk);
+  wave_lds_sync();
+  const int r = kk - pk.above;
+  if (pk.count <= 0 || pk.count > WAVE_LIST || pk.count < r) return 0ull;
+  int w = 0, wl = 0;
+  wave_stream(buf, n, [&](u64 v, int) {               // 0 = past the end (no key is 0)
+    const int b = v ? lb(v) : -1;
+    const bool up = b > pk.bin, at = b == pk.bin;
+    const u64 mu = ballot(up), ma = ballot(at);
+    if (up) put(v, w + lanes_below(mu));
+    if (at) list[wl + lanes_below(ma)] = v;
+    w += __popcll(mu);
+    wl += __popcll(ma);
+  });
+  wave_lds_sync();
+  const u64 T = wave_list_kth(list, wl, kk - w, hist);
+  wave_lds_sync();
+  for (int i0 = 0; i0 < wl; i0 += WAVE) {              // the rank bin's keys >= T
+    const int i = i0 + l;
+    const u64 v = i < wl ? list[i] : 0ull;
+    const bool keep = i < wl && v >= T;
+    const u64 m = ballot(keep);
+    if (keep) put(v, w + lanes_below(m));
+    w += __popcll(m);
+  }
+  wave_lds_sync();
+  return T;
+}
+
 // Keep the exact top-kk of buf[0..cnt) in place (cnt > kk); returns the kk-th
 // key.  Streams the buffer: the wave's MFMA operands stay in registers meanwhile.
 __device__ __forceinline__ u64 wave_compact(u64* buf, int cnt, int kk, uint32_t* hist, u64* list, float lo,
                                            float hi) {
+  wave_own_stores_visible();
+  lo = wave_min_f32(lo);
+  hi = wave_max_f32(hi);
+  const u64 Tb = wave_binned_select(buf, cnt, kk, hist, list, lo, hi,
+                                    [&](u64 v, int pos) { __builtin_nontemporal_store(v, &buf[pos]); });
+  if (Tb) return Tb;
   const u64 T = wave_select_kth_stream(buf, cnt, kk, hist, list, lo, hi);
   int w = 0;
   wave_stream(buf, cnt, [&](u64 v, int) {        // in order; writes never pass the reads
@@ -255,6 +312,12 @@ __device__ __forceinline__ int wave_emit_cand(const Slot& st, int kk, uint32_t* 
 // The same by streaming the buffer (any length; registers stay free).
 __device__ __forceinline__ int wave_emit_cand_stream(const Slot& st, int kk, uint32_t* hist, u64* list, int32_t* oi,
                                                      float* os) {
+  if (st.cnt > kk) {                                  // two passes when the bins narrow the rank
+    const float lo = wave_min_f32(st.lo), hi = wave_max_f32(st.hi);
+    if (wave_binned_select(st.cand, st.cnt, kk, hist, list, lo, hi,
+                           [&](u64 v, int pos) { emit_key(v, pos, kk, oi, os); }))
+      return kk;
+  }
   const u64 T = st.cnt > kk ? wave_select_kth_stream(st.cand, st.cnt, kk, hist, list, st.lo, st.hi) : 1ull;
   int w = 0;
   wave_stream(st.cand, st.cnt, [&](u64 v, int) {
