@@ -9,11 +9,11 @@ namespace csa {
 
 enum Mode { MODE_TOPK = 0, MODE_THRESHOLD = 1, MODE_INTERLEAVED = 2 };
 
-// Queries per workgroup in the prefill-family kernels: 4 waves x 1 query row.
+// Queries per workgroup in the generic prefill kernel: 4 waves x 1 query row.
 constexpr int PF_ROWS = 4;
 constexpr int PF_THREADS = 256;
 // Upper bound on the persistent prefill grid (2 workgroups per CU on 256 CUs);
-// each workgroup owns PF_ROWS candidate buffers in the workspace.
+// each workgroup owns one candidate buffer per query row in the workspace.
 constexpr int PF_MAX_GRID = 512;
 // Keys per LDS stage of the MFMA prefill kernel.
 constexpr int PF_KTILE = 64;

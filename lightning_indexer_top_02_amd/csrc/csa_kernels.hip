@@ -191,7 +191,7 @@ __device__ __forceinline__ void emit_key(u64 x, int pos, int kk, int32_t* oi, fl
 }
 
 // Candidate buffers up to this size are selected from registers: one load
-// pass with every load in flight instead of three latency-bound streaming
+// pass with every load in flight instead of two latency-bound streaming
 // passes.
 constexpr int EMIT_REGS = 66;
 
