@@ -112,6 +112,19 @@ def _select_case(case):
             k[b, s] = top
         p["k"] = csa_inputs.f32_to_bf16_bits(k)
         return p
+    if case == "one_wave_heavy":      # 100 planted keys all in one scan wave's keys: that wave's bound
+        # sits far above the others' and one select segment holds them.  With 1024- or 2048-key scan
+        # chunks of four waves, wave 0 of chunk 0 scores keys 128 j + i (i < 32, j < 8 or 16).
+        p = csa_inputs.make_decode(B=3, context=4 * 32768, topk=2048, n_planted=100, seed=58)
+        k = _bf16_to_f32(p["k"])
+        mine = np.array([128 * j + i for j in range(16) for i in range(32)])[:100]
+        for b in range(p["B"]):
+            planted = k[b, int(p["planted"][b, 0])].copy()
+            k[b, p["planted"][b]] = k[b, (p["planted"][b] + 1) % p["T"]]   # undo the spread plant
+            k[b, mine] = planted
+            p["planted"][b] = mine
+        p["k"] = csa_inputs.f32_to_bf16_bits(k)
+        return p
     if case == "noncausal":           # every key visible to every row, kv_len caps one sequence
         p = csa_inputs.make_decode(B=3, context=4 * 6000, topk=700, n_planted=8, S_q=4, seed=57)
         p["causal"] = False
@@ -122,16 +135,23 @@ def _select_case(case):
 
 
 @pytest.mark.parametrize("case", ["no_planted", "long_rows", "ragged_kv", "k_near_vis", "crowded_bin",
-                                  "noncausal"])
-def test_decode_select_paths(case):
+                                  "one_wave_heavy", "noncausal"])
+@pytest.mark.parametrize("chunk", [0, 2048])
+def test_decode_select_paths(case, chunk):
+    """Each case with the default scan chunks and with 2048-key chunks forced
+    (the small cases otherwise take 1024-key chunks)."""
     p = _select_case(case)
-    _say(f"decode select path case {case}: B={p['B']} S_q={p['S_q']} T={p['T']} k={p['topk']}")
-    idx, sc = _decode(p, return_scores=True)
+    _say(f"decode select path case {case} chunk={chunk}: B={p['B']} S_q={p['S_q']} T={p['T']} k={p['topk']}")
+    with L.test_options(decode_chunk=chunk):
+        idx, sc = _decode(p, return_scores=True)
     check_tolerance(p, np.arange(p["S_q"]), idx, sc, p["topk"])
     ref = _prefill(p)
     for b in range(p["B"]):
         for r in range(p["S_q"]):
             assert sorted(idx[b, r].tolist()) == sorted(ref[b, r].tolist()), f"row ({b},{r}) differs from prefill"
+    if case == "one_wave_heavy":
+        for b in range(p["B"]):
+            assert set(p["planted"][b].tolist()) <= set(idx[b, 0].tolist())
     if case == "crowded_bin":         # ties among the rest: the lowest indices win
         for b in range(p["B"]):
             s = int(p["planted"][b, 0])
