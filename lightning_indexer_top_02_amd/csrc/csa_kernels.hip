@@ -1199,12 +1199,26 @@ __global__ __launch_bounds__(DEC_SEL_THREADS) void decode_select_batch_kernel(De
 // Lane exchanges inside 16-lane rows through DPP (no LDS round trip):
 // quad_perm [1,0,3,2] and [2,3,0,1], then the mirrored half row and row, pair
 // every lane with one whose partial covers the other lanes of its 2, 4, 8 and
-// 16 group; the last step (lane ^ 16) goes through ds_bpermute.
+// 16 group; the last step (lane ^ 16) crosses rows with v_permlane16_swap.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+// The step between 16-lane rows (lane ^ 16): v_permlane16_swap with x in both
+// operands exchanges rows 1 and 3 of the first with rows 0 and 2 of the
+// second, so every lane ends with its own row's value in one result and the
+// neighbouring row's in the other; their max or sum is the butterfly step,
+// without an LDS round trip.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ uint32_t at_swz(int r, int col) {   // bf16 element (r, col) of a 128-wide tile
   return (uint32_t)(r * AT_CHUNK * 2 + ((((col >> 3) ^ (r & 15)) << 4) | ((col & 7) << 1)));
@@ -1299,7 +1313,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], dpp_f32<DPP_MIRROR>(red_v[e]));
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red_v[e] = fmaxf(red_v[e], __shfl_xor(red_v[e], 16, WAVE));
+      for (int e = 0; e < 16; ++e) red_v[e] = max_xor16(red_v[e]);
       if ((l & 31) == 0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) red[wv][rt * 32 + hrow(e)] = red_v[e];
@@ -1337,7 +1351,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) red_v[e] += dpp_f32<DPP_MIRROR>(red_v[e]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red_v[e] += __shfl_xor(red_v[e], 16, WAVE);
+      for (int e = 0; e < 16; ++e) red_v[e] = add_xor16(red_v[e]);
       if ((l & 31) == 0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) red[wv][rt * 32 + hrow(e)] = red_v[e];
