@@ -139,7 +139,7 @@ csa_status csa_index_topk_decode(const csa_problem* prob, int32_t topk, uint32_t
  * GPU it runs on until the process ends, so the call allocates nothing.
  * Supported: the decode fast path (bf16 q and k, H = 64, D = 128, S_q <=
  * CSA_MAX_DECODE_SQ) with a workspace need of at most the scratch size, i.e.
- * about B*S_q*(T+64)*4 bytes of scores plus 64 bytes per 1024 keys per row
+ * about B*S_q*(T+67)*4 bytes of scores plus 64 bytes per 1024 keys per row
  * (B*S_q = 32 rows at T = 32768 take 4.2 MB); larger problems and other
  * shapes return CSA_ERR_UNSUPPORTED with nothing enqueued.  The scratch needs
  * no initialisation.  Every call on one GPU uses that GPU's one array: calls

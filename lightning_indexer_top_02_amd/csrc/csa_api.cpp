@@ -177,7 +177,7 @@ DecodePlan plan_decode(const csa_problem* p, int kk, uint32_t flags) {
   d.chunk = decode_chunk(p, kk);
   d.nsplit = (p->T + d.chunk - 1) / d.chunk;
   d.nbw = d.nsplit * (csa::DEC_THREADS / 64);
-  d.score_bytes = align_up((size_t)p->B * p->S_q * (p->T + csa::DEC_PAD) * sizeof(float));
+  d.score_bytes = align_up((size_t)p->B * p->S_q * csa::dec_row_floats(p->T) * sizeof(float));
   d.bound_bytes = align_up((size_t)p->B * p->S_q * d.nbw * sizeof(uint4));
   d.sort_bytes = (flags & CSA_SORTED) ? align_up((size_t)p->B * p->S_q * kk * sizeof(float)) : 0;
   d.total = d.score_bytes + d.bound_bytes + d.sort_bytes;

@@ -59,7 +59,7 @@ struct DecodeArgs {
   int causal;
   unsigned long long thr_fixed;  // threshold mode: smallest surviving key (0: top-k mode)
   int32_t* out_count;   // threshold mode: survivors per row
-  float* scores;        // [B*S_q][T + DEC_PAD] fp32 workspace
+  float* scores;        // [B*S_q][dec_row_floats(T)] fp32 workspace
   uint4* bounds;        // [B*S_q][nbw] per-wave selection bounds {order bits, count, max order bits, 0}
   int nbw;              // bounds per row: DEC_THREADS / WAVE per key chunk
   int chunk;            // keys per scan workgroup: DEC_CHUNK or DEC_CHUNK_LONG
@@ -80,6 +80,9 @@ constexpr int DEC_CHUNK = 1024;        // keys per decode-scan workgroup
 constexpr int DEC_CHUNK_LONG = 2048;   // ... for long rows with enough workgroups (DecodeArgs::chunk)
 constexpr int DEC_RING = 3;            // key-row buffers per wave in the decode scan
 constexpr int DEC_PAD = 64;            // floats after each score row (stores of keys past the end)
+// Floats per row of the decode score workspace: T rounded up to a multiple of
+// 4 (16-byte aligned rows for the select's 16-byte loads) plus the pad.
+__host__ __device__ constexpr long long dec_row_floats(int T) { return (((long long)T + 3) & ~3ll) + DEC_PAD; }
 constexpr int DEC_SEL_THREADS = 1024;
 
 // Sparse attention over selected keys (H = 64 heads, Dk = Dv = 128, bf16).

@@ -795,7 +795,7 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
   // conflicts), which leaves the registers for a ring of DEC_RING key-row
   // buffers: DEC_RING - 1 steps (8 KB each per wave) stay in flight.
   __shared__ bf16x8 Als[2][8][WAVE];
-  float* out = a.scores + (size_t)row * (a.T + DEC_PAD);
+  float* out = a.scores + (size_t)row * dec_row_floats(a.T);
   const size_t kseq = (size_t)b * a.T;
   constexpr int STEP = 32, STRIDE = STEP * (DEC_THREADS / WAVE);
   auto load = [&](int base, bf16x8 (&bf)[8]) {
@@ -907,7 +907,8 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_score_batch_kernel(Deco
 
 // decode_select: one workgroup per query row; exact top-kk of the row's
 // dense scores.  Wave w holds the contiguous element range [w*2048, w*2048+2048)
-// in registers (element w*2048 + j*64 + lane in v[j]).
+// in registers (lane l's v[4i .. 4i+3] are elements w*2048 + 256*i + 4*l .. +3,
+// read with one 16-byte load).
 //
 // The scan's per-wave bounds give L = min_w P_w with at least sum_w c_w >= kk
 // keys at or above it, so the kk-th largest key scores >= L and only keys
@@ -969,7 +970,7 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
   const int tid = threadIdx.x, wv = tid / WAVE, l = tid & (WAVE - 1);
   const int row = blockIdx.x, b = row / a.S_q, i = row % a.S_q;
   const int vis = decode_visible(a, b, i);
-  const float* sc = a.scores + (size_t)row * (a.T + DEC_PAD);
+  const float* sc = a.scores + (size_t)row * dec_row_floats(a.T);
   int32_t* oi = a.out_idx + (size_t)row * a.kk;
   float* os = a.out_score ? a.out_score + (size_t)row * a.kk : nullptr;
   float* segv = segv_all + wv * DEC_SEG;
@@ -978,17 +979,22 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
   int w = 0;
   bool dense = vis > DEC_REG * DEC_SEL_THREADS;
   if (!dense) {
-    const int e0 = wv * (DEC_REG * WAVE) + l;
-    const int last = vis > 0 ? vis - 1 : 0;
+    // v[j] holds element el(j): lane l loads the 4 consecutive elements
+    // wv * 2048 + 256 * (j / 4) + 4 * l .. + 3 with one 16-byte load (a load
+    // instruction brings 1 KB of the row).
+    const int e0 = wv * (DEC_REG * WAVE) + 4 * l;
+    auto el = [&](int j) { return e0 + (j >> 2) * (4 * WAVE) + (j & 3); };
     // the row's bounds first: loads complete in order, so reducing them does
     // not wait for the score loads behind them
     const int nwr = (vis + a.chunk - 1) / a.chunk * (DEC_THREADS / WAVE);   // <= 128 here
     const uint4 bd = tid < nwr && vis > a.kk ? a.bounds[(size_t)row * a.nbw + tid] : make_uint4(~0u, 0u, 0u, 0u);
     float v[DEC_REG];
+    const int glast = vis > 0 ? (vis - 1) & ~3 : 0;   // last group holding a visible element
 #pragma unroll
-    for (int j = 0; j < DEC_REG; ++j) {               // every load in flight at once
-      const int s = e0 + j * WAVE;
-      v[j] = sc[s < vis ? s : last];
+    for (int j = 0; j < DEC_REG; j += 4) {            // every load in flight at once; a group
+      const int g = el(j);                            // past the row's end re-reads the last one
+      const float4 t = *(const float4*)(sc + (g < glast ? g : glast));   // (its elements are masked)
+      v[j] = t.x; v[j + 1] = t.y; v[j + 2] = t.z; v[j + 3] = t.w;
     }
     // Threshold mode: the survivors are the keys >= thr_fixed, i.e. scoring
     // >= sf (the smallest fp32 score above the threshold; the float compare
@@ -1001,7 +1007,7 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
     if (thr) {
       int mine = 0;
 #pragma unroll
-      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(e0 + j * WAVE < vis && v[j] >= sf));
+      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(el(j) < vis && v[j] >= sf));
       if (l == 0) wcnt[wv] = mine;
       __syncthreads();
       int tot = 0;
@@ -1013,7 +1019,7 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
     if (all) {                                        // every visible key (survivor), in element order
       int mine = 0;
 #pragma unroll
-      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(e0 + j * WAVE < vis && v[j] >= sf));
+      for (int j = 0; j < DEC_REG; ++j) mine += __popcll(ballot(el(j) < vis && v[j] >= sf));
       if (l == 0) wcnt[wv] = mine;
       __syncthreads();
       int off = 0, tot = 0;
@@ -1023,7 +1029,7 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
       }
 #pragma unroll
       for (int j = 0; j < DEC_REG; ++j) {
-        const int s = e0 + j * WAVE;
+        const int s = el(j);
         const bool keep = s < vis && v[j] >= sf;
         const u64 m = ballot(keep);
         if (keep) emit_key(make_key(v[j], (uint32_t)s), off + lanes_below(m), a.kk, oi, os);
@@ -1059,7 +1065,7 @@ __device__ __forceinline__ void decode_select_body(const DecodeArgs& a) {
         auto pack = [&](auto in_range) {
 #pragma unroll
           for (int j = 0; j < DEC_REG; ++j) {
-            const int s = e0 + j * WAVE;
+            const int s = el(j);
             const bool c = in_range(s) && v[j] >= lf;
             const u64 m = ballot(c);
             const int pos = cw + lanes_below(m);
