@@ -275,7 +275,7 @@ csa_status csa_union_rows(const int32_t* const* lists, const int32_t* widths, in
  *                          order), also for bf16 H = 64, D = 128.
  *   CSA_OPT_CAND_CAP       > 0: candidate keys held per query row between
  *                          compactions of the prefill kernels (raised to the
- *                          minimum 2*k + 64 when smaller); 0: 4*k + 64.
+ *                          minimum 2*k + 64 when smaller); 0: 12*k + 64.
  *   CSA_OPT_DECODE_CHUNK   1024 or 2048: keys per decode-scan workgroup;
  *                          0: chosen from the shape.
  * Errors: CSA_ERR_INVALID for an unknown option or a value outside its range

@@ -407,7 +407,7 @@ csa_status csa_index_topk_decode_noalloc(const csa_problem* prob, int32_t topk, 
     const DecodePlan d = plan_decode(prob, topk, flags);
     if (d.total > csa::NOALLOC_SCRATCH_BYTES)
       return fail(CSA_ERR_UNSUPPORTED, "problem needs %zu bytes of scratch, above the %zu this entry point holds "
-                  "(B*S_q*(T+64)*4 bytes of scores plus bounds); use csa_index_topk_decode with a workspace",
+                  "(B*S_q*(T+67)*4 bytes of scores plus bounds); use csa_index_topk_decode with a workspace",
                   d.total, csa::NOALLOC_SCRATCH_BYTES);
     void* ws = nullptr;
     const hipError_t e = csa::noalloc_scratch(&ws);
