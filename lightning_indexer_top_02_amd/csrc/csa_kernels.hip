@@ -765,9 +765,10 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs
 // ============================================================ decode
 //
 // decode_score: grid (nsplit, B*S_q).  Workgroup x scans keys
-// [x*chunk, (x+1)*chunk) of one query row; each wave takes 64-key steps.  The
-// key rows go straight from HBM into MFMA B operands (16 B per lane); the
-// query's 64x128 A operand and the lane's head weights stay in registers.
+// [x*chunk, (x+1)*chunk) of one query row; each wave takes 32-key steps.  The
+// key rows are read whole from HBM and reach the MFMA B operands through a
+// per-wave LDS tile; the query's 64x128 A operand sits in LDS and the lane's
+// head weights in registers.
 
 __device__ __forceinline__ int decode_visible(const DecodeArgs& a, int b, int i) {
   long long v = a.causal ? (a.q_pos0 + i) / a.m + 1 : (long long)a.T;
@@ -794,17 +795,29 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
   // copies two of the eight 16-deep slices; 16-byte reads without bank
   // conflicts), which leaves the registers for a ring of DEC_RING key-row
   // buffers: DEC_RING - 1 steps (8 KB each per wave) stay in flight.
+  // Key rows are read whole (1 KB of consecutive bytes per load instruction,
+  // with the non-temporal hint: each byte is used once) and pass through a
+  // per-wave LDS tile into the MFMA B layout.  In the tile, 16-byte piece p
+  // of step key c sits at slot 16c + (p ^ (c % 16)), so both the row-wise
+  // writes and the column-wise operand reads of 16 lanes spread over all
+  // banks.
   __shared__ bf16x8 Als[2][8][WAVE];
+  __shared__ u32x4 Kls[DEC_THREADS / WAVE][32 * 16];
   float* out = a.scores + (size_t)row * dec_row_floats(a.T);
   const size_t kseq = (size_t)b * a.T;
   constexpr int STEP = 32, STRIDE = STEP * (DEC_THREADS / WAVE);
-  auto load = [&](int base, bf16x8 (&bf)[8]) {
-    int s = base + (l & 31);
-    s = s < end ? s : end - 1;
-    const bf16x8* src = (const bf16x8*)(K + (kseq + s) * MD);
+  // Instruction i of a step reads keys base + 4i .. +3: lane l takes piece
+  // l % 16 of key base + 4i + l / 16.
+  auto load = [&](int base, u32x4 (&bf)[8]) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) bf[kk] = src[2 * kk + (l >> 5)];
+    for (int i = 0; i < 8; ++i) {
+      int s = base + 4 * i + (l >> 4);
+      s = s < end ? s : end - 1;
+      bf[i] = __builtin_nontemporal_load((const u32x4*)(K + (kseq + s) * MD) + (l & 15));
+    }
   };
+  u32x4* kt = Kls[wv];
+  auto slot = [](int c, int p) { return 16 * c + (p ^ (c & 15)); };
   static_assert(CH % STRIDE == 0, "decode chunk must be whole steps");
   static_assert(DEC_THREADS / WAVE * 2 == 8, "each wave copies two query slices");
   constexpr int NSTEP = CH / STRIDE;
@@ -816,7 +829,7 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) qa[rt][h] = src[2 * (2 * wv + h) + (l >> 5)];
   }
-  bf16x8 bb[DEC_RING][8];
+  u32x4 bb[DEC_RING][8];
 #pragma unroll
   for (int st = 0; st < DEC_RING - 1; ++st) load(base0 + st * STRIDE, bb[st]);
   float wl[2][16];
@@ -838,11 +851,19 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
     if (st + DEC_RING - 1 < NSTEP) load(base0 + (st + DEC_RING - 1) * STRIDE, bb[(st + DEC_RING - 1) % DEC_RING]);
     asm volatile("" ::: "memory");                    // re-read the A slices from LDS every step
     __builtin_amdgcn_sched_barrier(0);
+    // the step's rows into the tile, then B operands: lane l holds 16 bytes
+    // (d = 8 * (2 * kk + l / 32) .. + 7) of key l % 32; a wave's LDS accesses
+    // complete in order, so the tile is reused without a barrier
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kt[slot(4 * i + (l >> 4), l & 15)] = bb[st % DEC_RING][i];
+    bf16x8 bk[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) bk[kk] = __builtin_bit_cast(bf16x8, kt[slot(l & 31, 2 * kk + (l >> 5))]);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Als[rt][kk][l], bb[st % DEC_RING][kk], acc[rt], 0, 0, 0);
+      for (int rt = 0; rt < 2; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Als[rt][kk][l], bk[kk], acc[rt], 0, 0, 0);
     float ps = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
