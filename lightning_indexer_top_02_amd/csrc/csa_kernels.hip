@@ -770,6 +770,11 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_generic_kernel(PrefillArgs
 // per-wave LDS tile; the query's 64x128 A operand sits in LDS and the lane's
 // head weights in registers.
 
+// Slot of 16-byte piece p (0..15) of key c (0..31) in a per-wave 8 KB tile
+// of 32 key rows: the row-wise writes and the column-wise MFMA B-operand reads
+// of 16 lanes both cover all banks.
+__device__ __forceinline__ int key_tile_slot(int c, int p) { return 16 * c + (p ^ (c & 15)); }
+
 __device__ __forceinline__ int decode_visible(const DecodeArgs& a, int b, int i) {
   long long v = a.causal ? (a.q_pos0 + i) / a.m + 1 : (long long)a.T;
   if (v > a.T) v = a.T;
@@ -817,7 +822,6 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
     }
   };
   u32x4* kt = Kls[wv];
-  auto slot = [](int c, int p) { return 16 * c + (p ^ (c & 15)); };
   static_assert(CH % STRIDE == 0, "decode chunk must be whole steps");
   static_assert(DEC_THREADS / WAVE * 2 == 8, "each wave copies two query slices");
   constexpr int NSTEP = CH / STRIDE;
@@ -855,10 +859,10 @@ __device__ __forceinline__ void decode_score_body(const DecodeArgs& a) {
     // (d = 8 * (2 * kk + l / 32) .. + 7) of key l % 32; a wave's LDS accesses
     // complete in order, so the tile is reused without a barrier
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kt[slot(4 * i + (l >> 4), l & 15)] = bb[st % DEC_RING][i];
+    for (int i = 0; i < 8; ++i) kt[key_tile_slot(4 * i + (l >> 4), l & 15)] = bb[st % DEC_RING][i];
     bf16x8 bk[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) bk[kk] = __builtin_bit_cast(bf16x8, kt[slot(l & 31, 2 * kk + (l >> 5))]);
+    for (int kk = 0; kk < 8; ++kk) bk[kk] = __builtin_bit_cast(bf16x8, kt[key_tile_slot(l & 31, 2 * kk + (l >> 5))]);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
