@@ -125,6 +125,11 @@ def _select_case(case):
             p["planted"][b] = mine
         p["k"] = csa_inputs.f32_to_bf16_bits(k)
         return p
+    if case == "odd_T":               # T and the visible counts not multiples of 4: score rows padded
+        # to a multiple of 4 floats, 16-byte select loads over a partial last group, clamped key rows
+        p = csa_inputs.make_decode(B=3, context=4 * 4099, topk=512, n_planted=8, seed=59)
+        p["kv_len"] = np.array([4099, 4097, 2051], dtype=np.int32)
+        return p
     if case == "noncausal":           # every key visible to every row, kv_len caps one sequence
         p = csa_inputs.make_decode(B=3, context=4 * 6000, topk=700, n_planted=8, S_q=4, seed=57)
         p["causal"] = False
@@ -135,7 +140,7 @@ def _select_case(case):
 
 
 @pytest.mark.parametrize("case", ["no_planted", "long_rows", "ragged_kv", "k_near_vis", "crowded_bin",
-                                  "one_wave_heavy", "noncausal"])
+                                  "one_wave_heavy", "odd_T", "noncausal"])
 @pytest.mark.parametrize("chunk", [0, 2048])
 def test_decode_select_paths(case, chunk):
     """Each case with the default scan chunks and with 2048-key chunks forced
