@@ -124,3 +124,45 @@ def test_batched_threshold_sorted_with_scores_eight_layers():
                                               sorted=True, return_scores=True)
         torch.cuda.synchronize()
         assert torch.equal(cnt[li], rc) and torch.equal(idx[li], ri) and torch.equal(sco[li], rs), f"layer {li}"
+
+
+def test_batched_threshold_decode_workload_vs_oracle():
+    """Three layers at the decode workload (B=32, T=32768, tau = 0.5, cap
+    2048) in one batched launch, checked against the fp64 oracle on sampled
+    rows of every layer: the survivor count within the bf16 tolerance band
+    around the threshold, and the kept keys the survivors' best 2048 up to
+    the band around the 2048-th (or every survivor when fewer survive)."""
+    from gpu_common import REL, FLOOR_DIV
+    pd = [csa_inputs.make_decode(seed=s) for s in (1007, 1008, 1009)]
+    layers = [(torch.from_numpy(p["q"].view(np.int16)).view(torch.bfloat16).cuda(),
+               torch.from_numpy(p["k"].view(np.int16)).view(torch.bfloat16).cuda(),
+               torch.from_numpy(p["w"]).cuda()) for p in pd]
+    cap, tau = 2048, 0.5
+    _say("batched threshold selection at the decode workload: 3 layers vs the oracle on sampled rows")
+    got = L.index_threshold_select_layers(layers, cap, prob_threshold=tau, m=pd[0]["m"], q_pos0=pd[0]["q_pos0"])
+    torch.cuda.synchronize()
+    theta = oracle.logit_threshold(tau, 0.0)
+    for li, (p, (gi, gc)) in enumerate(zip(pd, got)):
+        idx, cnt = gi.cpu().numpy(), gc.cpu().numpy()
+        scorer = oracle.RowScorer(p)
+        for b in (0, 17, 31):
+            I = scorer(b, 0)
+            floor = float(np.sqrt(np.mean(I * I))) / FLOOR_DIV
+            band = REL * max(abs(theta), floor)
+            true_cnt = int((I > theta).sum())
+            near = int((np.abs(I - theta) <= band).sum())
+            assert abs(int(cnt[b, 0]) - true_cnt) <= near, f"layer {li} row {b}: count {cnt[b, 0]} vs {true_cnt}"
+            n = min(cap, int(cnt[b, 0]))
+            sel = idx[b, 0, :n]
+            assert (idx[b, 0, n:] == -1).all() and len(set(sel.tolist())) == n
+            surv = oracle.order_desc(I, np.nonzero(I > theta)[0])
+            if true_cnt > cap:
+                ref = surv[:cap]
+                vc = I[ref].min()
+                bc = REL * max(abs(vc), floor)
+                for s_ in set(sel.tolist()) ^ set(ref.tolist()):
+                    assert abs(I[s_] - vc) <= bc, f"layer {li} row {b}: index {s_} outside the band"
+            else:
+                for s_ in set(sel.tolist()) ^ set(surv.tolist()):
+                    assert abs(I[s_] - theta) <= band, f"layer {li} row {b}: survivor {s_} missing or extra"
+            assert set(p["planted"][b].tolist()) <= set(sel.tolist()), f"layer {li} row {b}: a planted key is missing"
