@@ -66,11 +66,16 @@ def _integer_decode(B=3, S_q=2, T=3000, topk=200, seed=3):
     return p
 
 
-@pytest.mark.parametrize("case", ["plain", "kv_len", "sorted", "few_visible", "fp32_fallback"])
+@pytest.mark.parametrize("case", ["plain", "kv_len", "sorted", "few_visible", "fp32_fallback", "max_rows",
+                                  "tiny_T"])
 def test_decode_exact_cases(case):
     p = _integer_decode()
     kw = {}
-    if case == "kv_len":
+    if case == "max_rows":                     # the most query rows per sequence the decode path takes
+        p = _integer_decode(B=2, S_q=16, T=2500, topk=300, seed=11)
+    elif case == "tiny_T":                     # fewer keys than one scan step, and than k
+        p = _integer_decode(B=3, S_q=3, T=5, topk=8, seed=12)
+    elif case == "kv_len":
         p["kv_len"] = np.array([3000, 1234, 150], dtype=np.int32)
     elif case == "sorted":
         kw["sorted"] = True
