@@ -291,12 +291,48 @@ def bench_decode(args, torch, L, csa_inputs, R):
     ms = total_ms / steps
     gbps = nbytes / (ms * 1e-3) / 1e9
     _log(f"decode: {p['name']}: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s ({gbps / R.PEAK_HBM_GBPS:.1%} of HBM peak)")
+    split = _decode_kernel_split(torch, call, steps, nbytes, R)
     del q, ks, k0, w, out, ws
     torch.cuda.empty_cache()
     return dict(value=round(gbps, 1), unit="GB/s", ms_per_call=round(ms, 5),
                 frac_hbm_peak=round(gbps / R.PEAK_HBM_GBPS, 4), bytes_per_call=nbytes,
-                launch_ms_avg=round(avg_ms, 5), calls=steps, key_copies_rotated=4,
+                launch_ms_avg=round(avg_ms, 5), calls=steps, key_copies_rotated=4, kernels=split,
                 workload="decode B=32 x 1 query, context 131072 (T=32768), H_I=64, d_I=128, k=2048, bf16")
+
+
+def _decode_kernel_split(torch, call, calls, nbytes, R):
+    """Device time of each decode kernel over `calls` back-to-back calls,
+    from the HIP runtime's kernel records (torch.profiler over ROCTracer),
+    and the key scan's own rate: the algorithmic bytes of a decode call
+    (keys, query, weights, output indices) over the scan kernel's average
+    duration.  None if the profiler yields no records for the kernels."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for i in range(calls):
+                call(i)
+            torch.cuda.synchronize()
+        dur = {}
+        for e in prof.events():
+            for kname in ("decode_score_kernel", "decode_select_kernel"):
+                if kname in e.name:
+                    dur.setdefault(kname, []).append(e.device_time_total)
+        scan, sel = dur.get("decode_score_kernel"), dur.get("decode_select_kernel")
+        if not scan or not sel:
+            return None
+        scan_us, sel_us = sum(scan) / len(scan), sum(sel) / len(sel)
+        gbps = nbytes / (scan_us * 1e-6) / 1e9
+        _log(f"decode kernels: key scan {scan_us:.1f} us ({gbps:.0f} GB/s, {gbps / R.PEAK_HBM_GBPS:.1%} of HBM peak), "
+             f"select {sel_us:.1f} us")
+        return dict(source="torch.profiler (ROCTracer) device time per kernel", calls=len(scan),
+                    key_scan={"kernel": "decode_score_kernel<2048>", "us_avg": round(scan_us, 2),
+                              "value": round(gbps, 1), "unit": "GB/s",
+                              "frac_hbm_peak": round(gbps / R.PEAK_HBM_GBPS, 4)},
+                    select={"kernel": "decode_select_kernel", "us_avg": round(sel_us, 2)})
+    except Exception as exc:                          # the split is extra; the call's timing stands without it
+        _log(f"decode kernel split unavailable: {exc}")
+        return None
 
 
 def bench_read_stream(args, torch, R):
